@@ -1,0 +1,236 @@
+"""Plain, slow, obviously-correct CPU oracle (numpy) for the SVDQuant linear layer.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module. It shares no code, table or helper with the GPU library.
+
+What it computes (sources are the pages this project follows):
+
+* The SVDQuant overview figure of the Nunchaku README ("Method > Quantization method - SVDQuant",
+  stages 1-3): outliers are migrated from the activations into the weights by a per-channel
+  smoothing (X_hat = X diag(lambda)^-1, W_hat = diag(lambda) W); W_hat is split by a truncated SVD
+  into a low-rank part L1 L2 kept in 16 bits and a residual R = W_hat - L1 L2 that is quantized
+  to 4 bits together with X_hat. The layer is therefore
+
+      Y = X_hat L1 L2 + dequant(Q4(X_hat) Q4(R)) + b.
+
+* The engine-design figure of the same README ("Nunchaku engine design", panels (a) and (b)):
+  the down projection X_hat L1 shares its input with the activation quantizer and the up
+  projection shares its output with the 4-bit product. Fusion changes no value, so the oracle
+  computes each piece separately.
+
+* The Diffusers blog on Nunchaku Lite ("From SVDQuant to Nunchaku Lite" and the
+  ``quantization_config`` example): ``svdq_w4a4`` layers with a rank-32 low-rank branch for
+  attention/MLP, ``awq_w4a16`` layers (int4 weights, group 64, 16-bit activations) for the
+  modulation / adaptive-norm projections, compute dtype bfloat16.
+
+Readings where the pages are silent (each is a documented choice, applied identically here and
+on the GPU): symmetric INT4 with one float32 scale per group of 64 consecutive inputs along K;
+scale = float32(absmax) / float32(7) with IEEE division; code = clamp(round_half_even(x / scale),
+-8, 7) with an IEEE float32 division; a group whose computed scale is 0 gets scale 0 and codes 0;
+X_hat = float32(x) * float32(1/lambda) (one float32 multiply); the down projection consumes
+bf16(X_hat) and its result T is stored as bf16; the output is rounded to bf16. The W4A16 scale
+is bf16(float32(absmax)/7) and its codes are computed against that rounded scale.
+The main product is evaluated in float64 (the exact integer group sums times the float32
+scales), the smoothing/SVD preparation in float64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64  # INT4 group size along K (quantization_config of the Diffusers blog: group_size 64 for int4)
+QMIN, QMAX = -8, 7
+
+__all__ = [
+    "GROUP", "bf16_round", "smoothing_factors", "svdq_decompose", "int4_quantize_rows",
+    "quantize_weights_w4a4", "smooth_activations", "quantize_activations", "lowrank_down",
+    "group_sums", "dequant_product", "svdq_linear", "svdq_layer", "quantize_weights_w4a16",
+    "awq_linear",
+]
+
+
+# ----------------------------------------------------------------------------------------------
+# 16-bit storage
+# ----------------------------------------------------------------------------------------------
+def bf16_round(a) -> np.ndarray:
+    """float32 -> nearest bfloat16 (ties to even), returned as float32 values.
+
+    Works on the float32 bit pattern: add 0x7FFF plus the lowest kept bit, then clear the low
+    16 bits. Inputs are finite (non-finite values are outside this oracle's domain).
+    """
+    f = np.ascontiguousarray(a, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)) << np.uint64(16)
+    return r.astype(np.uint32).view(np.float32).reshape(f.shape)
+
+
+# ----------------------------------------------------------------------------------------------
+# Offline preparation (overview figure, stages 2 and 3)
+# ----------------------------------------------------------------------------------------------
+def smoothing_factors(x: np.ndarray, w: np.ndarray):
+    """Per-input-channel smoothing (stage 2 of the SVDQuant overview figure).
+
+    lambda_k = sqrt(max_m |x[m,k]| / max_n |w[k,n]|) in float64 (the migration-strength-1/2 rule of
+    SmoothQuant, which the README lists as the related work this stage builds on); lambda_k = 1
+    when either maximum is 0. The runtime carries inv_k = float32(1/lambda_k) and the weights are
+    scaled by lambda'_k = 1/float64(inv_k), so that X diag(inv) diag(lambda') W = X W exactly in
+    real arithmetic.
+    Returns (inv float32 [K], lam_prime float64 [K]).
+    """
+    xmax = np.max(np.abs(x.astype(np.float64)), axis=0)
+    wmax = np.max(np.abs(w.astype(np.float64)), axis=1)
+    lam = np.ones(x.shape[1], dtype=np.float64)
+    ok = (xmax > 0) & (wmax > 0)
+    lam[ok] = np.sqrt(xmax[ok] / wmax[ok])
+    inv = (1.0 / lam).astype(np.float32)
+    lam_prime = 1.0 / inv.astype(np.float64)
+    return inv, lam_prime
+
+
+def svdq_decompose(x: np.ndarray, w: np.ndarray, rank: int):
+    """Smoothing + truncated SVD + residual (stages 2-3 of the SVDQuant overview figure).
+
+    x: float32 [M, K] activations used for calibration; w: float32 [K, N] weights (x @ w).
+    W_hat = diag(lambda') w; W_hat = U S V^T; L1 = U_r S_r, L2 = V_r^T (float64).
+    The runtime factors are bf16(L1), bf16(L2); the residual that gets quantized is
+    R = W_hat - bf16(L1) bf16(L2), computed in float64 and stored as float32.
+    """
+    inv, lam_prime = smoothing_factors(x, w)
+    w_hat = lam_prime[:, None] * w.astype(np.float64)
+    u, s, vt = np.linalg.svd(w_hat, full_matrices=False)
+    l1 = u[:, :rank] * s[:rank]
+    l2 = vt[:rank, :]
+    l1_b = bf16_round(l1.astype(np.float32))
+    l2_b = bf16_round(l2.astype(np.float32))
+    resid = (w_hat - l1_b.astype(np.float64) @ l2_b.astype(np.float64)).astype(np.float32)
+    return {"inv": inv, "lam_prime": lam_prime, "w_hat": w_hat, "sigma": s, "l1": l1, "l2": l2,
+            "l1_bf16": l1_b, "l2_bf16": l2_b, "resid": resid}
+
+
+# ----------------------------------------------------------------------------------------------
+# Symmetric INT4, one float32 scale per group of 64 along the reduction axis
+# ----------------------------------------------------------------------------------------------
+def int4_quantize_rows(v: np.ndarray):
+    """Quantize each row of float32 ``v`` [rows, K] in groups of 64 consecutive entries.
+
+    scale = float32(absmax) / float32(7) (IEEE); code = clamp(rint_even(v / scale), -8, 7) with
+    an IEEE float32 division; a group whose scale is 0 gets codes 0.
+    Returns (codes int8 [rows, K], scales float32 [rows, K/64]).
+    """
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    rows, K = v.shape
+    assert K % GROUP == 0
+    G = K // GROUP
+    vg = v.reshape(rows, G, GROUP)
+    amax = np.max(np.abs(vg), axis=2)                               # exact
+    scale = (amax / np.float32(7.0)).astype(np.float32)             # float32 / float32: IEEE
+    codes = np.zeros((rows, G, GROUP), dtype=np.int8)
+    nz = scale != 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = vg / scale[:, :, None]                                  # float32 division
+    q = np.clip(np.rint(q), QMIN, QMAX)                             # round half to even, clamp
+    codes[nz] = q[nz].astype(np.int8)
+    return codes.reshape(rows, K), scale
+
+
+def quantize_weights_w4a4(resid: np.ndarray):
+    """Q4 of the residual R [K, N] along K, per output column.
+
+    Returns (codes int8 [K, N], scales float32 [K/64, N]).
+    """
+    c, s = int4_quantize_rows(np.ascontiguousarray(resid.T))
+    return np.ascontiguousarray(c.T), np.ascontiguousarray(s.T)
+
+
+def smooth_activations(x: np.ndarray, inv: np.ndarray) -> np.ndarray:
+    """X_hat = float32(x) * inv (one float32 multiply per element, round to nearest even)."""
+    return (x.astype(np.float32) * inv.astype(np.float32)[None, :]).astype(np.float32)
+
+
+def lowrank_down(x_hat: np.ndarray, l1_bf16: np.ndarray) -> np.ndarray:
+    """T = bf16( bf16(X_hat) @ bf16(L1) ): the 16-bit down projection (engine figure (a)/(b))."""
+    xh16 = bf16_round(x_hat).astype(np.float64)
+    return bf16_round((xh16 @ l1_bf16.astype(np.float64)).astype(np.float32))
+
+
+def quantize_activations(x: np.ndarray, inv: np.ndarray, l1_bf16=None):
+    """What the fused activation step produces: (codes int8 [M,K], scales float32 [K/64, M], T or None).
+
+    Codes/scales: Q4 of X_hat per token along K. T: the rank-r down projection of X_hat.
+    """
+    xh = smooth_activations(x, inv)
+    codes, sc = int4_quantize_rows(xh)
+    t = None if l1_bf16 is None or l1_bf16.shape[1] == 0 else lowrank_down(xh, l1_bf16)
+    return codes, np.ascontiguousarray(sc.T), t
+
+
+# ----------------------------------------------------------------------------------------------
+# The W4A4 product and the layer
+# ----------------------------------------------------------------------------------------------
+def group_sums(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """P[g, m, n] = sum_{k in group g} qa[m, k] * qw[k, n], exact integers (int64)."""
+    M, K = qa.shape
+    G = K // GROUP
+    a = qa.astype(np.int64).reshape(M, G, GROUP)
+    b = qw.astype(np.int64).reshape(G, GROUP, -1)
+    return np.stack([a[:, g, :] @ b[g] for g in range(G)], axis=0)
+
+
+def dequant_product(qa, sa, qw, sw) -> np.ndarray:
+    """dequant(Q4(X_hat) Q4(R)) = (qa * sa) @ (qw * sw) in float64.
+
+    qa int8 [M,K], sa float32 [K/64, M], qw int8 [K,N], sw float32 [K/64, N].
+    """
+    a = qa.astype(np.float64) * np.repeat(sa.T.astype(np.float64), GROUP, axis=1)
+    b = qw.astype(np.float64) * np.repeat(sw.astype(np.float64), GROUP, axis=0)
+    return a @ b
+
+
+def svdq_linear(qa, sa, qw, sw, t=None, l2_bf16=None, bias=None):
+    """Y = dequant(Q4(X_hat) Q4(R)) + T L2 + b, returned as (float64, bf16-rounded float32)."""
+    y = dequant_product(qa, sa, qw, sw)
+    if t is not None and l2_bf16 is not None and l2_bf16.shape[0] > 0:
+        y = y + t.astype(np.float64) @ l2_bf16.astype(np.float64)
+    if bias is not None:
+        y = y + bias.astype(np.float64)[None, :]
+    return y, bf16_round(y.astype(np.float32))
+
+
+def svdq_layer(x, inv, l1_bf16, l2_bf16, resid, bias=None):
+    """The whole layer from its prepared inputs; returns a dict of every intermediate."""
+    qa, sa, t = quantize_activations(x, inv, l1_bf16)
+    qw, sw = quantize_weights_w4a4(resid)
+    y64, y = svdq_linear(qa, sa, qw, sw, t, l2_bf16, bias)
+    return {"qa": qa, "sa": sa, "t": t, "qw": qw, "sw": sw, "y64": y64, "y": y}
+
+
+# ----------------------------------------------------------------------------------------------
+# W4A16 (AWQ-style) projection: int4 weights, group 64, bf16 scales, 16-bit activations
+# ----------------------------------------------------------------------------------------------
+def quantize_weights_w4a16(w: np.ndarray):
+    """int4 group-64 weights with bf16 scales: s = bf16(float32(absmax)/7); codes against s.
+
+    w float32 [K, N]. Returns (codes int8 [K, N], scales float32 [K/64, N] holding bf16 values).
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    K, N = w.shape
+    G = K // GROUP
+    wg = w.reshape(G, GROUP, N)
+    amax = np.max(np.abs(wg), axis=1)
+    s = bf16_round((amax / np.float32(7.0)).astype(np.float32))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = wg / s[:, None, :]
+    q = np.clip(np.rint(q), QMIN, QMAX)
+    codes = np.zeros((G, GROUP, N), dtype=np.int8)
+    nz = np.broadcast_to((s != 0)[:, None, :], q.shape)
+    codes[nz] = q[nz].astype(np.int8)
+    return codes.reshape(K, N), s
+
+
+def awq_linear(x, codes, scales, bias=None):
+    """Y = x @ (codes * scales) + b in float64; returns (float64, bf16-rounded float32)."""
+    wdq = codes.astype(np.float64) * np.repeat(scales.astype(np.float64), GROUP, axis=0)
+    y = x.astype(np.float64) @ wdq
+    if bias is not None:
+        y = y + bias.astype(np.float64)[None, :]
+    return y, bf16_round(y.astype(np.float32))
