@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of the SVDQuant W4A4 + low-rank hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  (a) svdq_quantize_act  on the MLP up projection, M=4608 tokens, K=3072, r=32
+  (b) svdq_linear_w4a4   M=4608, K=3072, N=12288, r=32 (int8 MFMA + fused bf16 low-rank epilogue)
+  (c) awq_linear_w4a16   adaLN modulation projection, M=16, K=3072, N=18432
+Inputs are resident in HBM before timing starts. Buffer sets rotate so that every step reads
+its activations / W4A16 weights from HBM rather than the 256 MB Infinity Cache.
+
+Prints one JSON line. ``value`` = algorithmic operations of the step / step time, in TOPS
+(int8-MFMA ops 2MNK of (b) + bf16 low-rank flops 2Mr(K+N) + W4A16 flops 2MNK of (c)).
+``roofline`` covers the dominant kernel (b): 2MNK / its average launch time (HIP events on the
+launch stream), against the MI355X dense int8 MFMA peak.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5033.2     # 256 CU x 2.4 GHz x 8192 int8 ops / clk / CU (published 5.0 POP/s dense)
+HBM_PEAK_GBS = 8000.0
+METRIC = "W4A4+low-rank linear TOPS (M4608 K3072 N12288 r32) & % int8 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=10, help="buffer sets cycled through (>256 MB total)")
+    ap.add_argument("--config", default="up", help="W4A4 workload from synth.CONFIGS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4608, help="token rows in the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(name: str) -> str:
+    with open(os.path.join(ROOT, "quantized_gemm_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when it was taken on the
+    current kernel source (same hash); otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    h = kernel_source_hash(kernel_file)
+    for line in open(path):
+        parts = line.split()
+        if len(parts) >= 4 and parts[0] == kernel_file and parts[1] == workload and parts[2] == h:
+            return float(parts[3])
+    return None
+
+
+def cpu_baseline(cfg, awq_cfg, rows: int):
+    """The oracle, as it stands, on a bounded sample of the same step (first ``rows`` tokens)."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+
+    inp = synth.make_layer_inputs(cfg, M=rows)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    b = synth.f32_from_bf16_bits(inp["bias"])
+    d = oracle.svdq_decompose(x, w, cfg.rank)          # offline preparation: not timed
+    qw, sw = oracle.quantize_weights_w4a4(d["resid"])
+    ainp = synth.make_layer_inputs(awq_cfg)
+    ax = synth.f32_from_bf16_bits(ainp["x"])
+    acodes, ascales = oracle.quantize_weights_w4a16(synth.f32_from_bf16_bits(ainp["w"]))
+    t0 = time.perf_counter()
+    qa, sa, t = oracle.quantize_activations(x, d["inv"], d["l1_bf16"])
+    oracle.svdq_linear(qa, sa, qw, sw, t, d["l2_bf16"], b)
+    oracle.awq_linear(ax, acodes, ascales, None)
+    dt = time.perf_counter() - t0
+    ops = 2.0 * rows * cfg.N * cfg.K + 2.0 * rows * cfg.rank * (cfg.K + cfg.N) + \
+        2.0 * awq_cfg.M * awq_cfg.N * awq_cfg.K
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{rows} of {cfg.M} tokens of the {cfg.name} layer (activation quantization, float64 "
+                      f"dequantized product, low-rank, bias) + the full W4A16 projection M={awq_cfg.M}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards by tokens or output columns with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import quantized_gemm_amd as q
+    from quantized_gemm_amd import prep
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    q.load_library()
+    q.svdq_check_device()
+
+    cfg = synth.CONFIGS[args.config]
+    awq_cfg = synth.CONFIGS["awq"]
+    M, K, N, r = cfg.M, cfg.K, cfg.N, cfg.rank
+    log(f"[bench] generating {cfg.name} M={M} K={K} N={N} r={r}")
+    inp = synth.make_layer_inputs(cfg)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    t0 = time.time()
+    d = prep.decompose(x, w, r)
+    log(f"[bench] offline decomposition {time.time() - t0:.1f}s; packing")
+    qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, d["resid"])
+    l1t, l2t = q.svdq_pack_lowrank(d["l1"], d["l2"]) if r else (None, None)
+    ainp = synth.make_layer_inputs(awq_cfg)
+    aqw, ascl = q.svdq_pack_weights(q.SVDQ_FMT_W4A16_BF16SCALE, synth.f32_from_bf16_bits(ainp["w"]))
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    R = max(1, args.rotate)
+    xs = [bf16_dev(inp["x"]) for _ in range(R)]
+    inv = torch.from_numpy(d["inv_smooth"]).to(dev)
+    qw_d, sw_d = torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev)
+    l1t_d = bf16_dev(l1t) if r else None
+    l2t_d = bf16_dev(l2t) if r else None
+    bias_d = bf16_dev(inp["bias"])
+    qact = [torch.empty((M, K // 2), dtype=torch.uint8, device=dev) for _ in range(R)]
+    asc = [torch.empty((K // 64, M), dtype=torch.float32, device=dev) for _ in range(R)]
+    tl = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) if r else None for _ in range(R)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ax = bf16_dev(ainp["x"])
+    aqws = [torch.from_numpy(aqw).to(dev) for _ in range(R)]
+    ascl_d = bf16_dev(ascl)
+    ay = torch.empty((awq_cfg.M, awq_cfg.N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(s, ev=None):
+        k = s % R
+        if ev is not None:
+            ev[0].record(stream)
+        q.svdq_quantize_act(xs[k], inv, l1t_d, qact[k], asc[k], tl[k], stream=sh)
+        if ev is not None:
+            ev[1].record(stream)
+        q.svdq_linear_w4a4(qact[k], asc[k], qw_d, sw_d, tl[k], l2t_d, bias_d, y, stream=sh)
+        if ev is not None:
+            ev[2].record(stream)
+        q.awq_linear_w4a16(ax, aqws[k], ascl_d, None, ay, stream=sh)
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    start.record(stream)
+    for s in range(args.steps):
+        step(s, evs[s])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    t_a = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_b = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    t_c = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    gemm_ops = 2.0 * M * N * K
+    lr_flops = 2.0 * M * r * (K + N)
+    awq_flops = 2.0 * awq_cfg.M * awq_cfg.N * awq_cfg.K
+    step_ops = gemm_ops + lr_flops + awq_flops
+    value = step_ops / (ms_step * 1e-3) / 1e12
+    achieved_b = gemm_ops / (t_b * 1e-3) / 1e12
+    bytes_a = M * K * 2 + M * K // 2 + (K // 64) * M * 4 + M * r * 2 + (r * K * 2) + K * 4
+    bytes_c = awq_cfg.N * awq_cfg.K // 2 + (awq_cfg.K // 64) * awq_cfg.N * 2 + awq_cfg.M * awq_cfg.K * 2 + \
+        awq_cfg.M * awq_cfg.N * 2
+    traffic = load_traffic("w4a4_gemm.hip", cfg.name)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"svdq_w4a4 {cfg.name} M{M} K{K} N{N} r{r} + awq_w4a16 M{awq_cfg.M} "
+                               f"K{awq_cfg.K} N{awq_cfg.N}", "M": M, "K": K, "N": N, "rank": r, "group": 64,
+                   "awq": [awq_cfg.M, awq_cfg.K, awq_cfg.N], "rotating_buffer_sets": R},
+        "roofline": {"bound": "mfma", "achieved": round(achieved_b, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved_b / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                     "kernel": "w4a4_gemm_kernel (svdq_linear_w4a4)", "ops_per_launch": gemm_ops},
+        "kernels": {
+            "svdq_quantize_act_us": round(t_a * 1e3, 2),
+            "svdq_quantize_act_GBs": round(bytes_a / (t_a * 1e-3) / 1e9, 1),
+            "svdq_linear_w4a4_us": round(t_b * 1e3, 2),
+            "svdq_linear_w4a4_TOPS": round(achieved_b, 2),
+            "awq_linear_w4a16_us": round(t_c * 1e3, 2),
+            "awq_linear_w4a16_GBs": round(bytes_c / (t_c * 1e-3) / 1e9, 1),
+            "layer_TOPS_a_plus_b": round(gemm_ops / ((t_a + t_b) * 1e-3) / 1e12, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (oracle) on {args.cpu_rows} rows")
+        out["cpu_baseline"] = cpu_baseline(cfg, awq_cfg, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * svdq.h -- C ABI of the MI355X (gfx950) SVDQuant W4A4 + low-rank linear and W4A16 projection.
+ *
+ * The layer (Nunchaku README, "Method > Quantization method - SVDQuant", overview figure, stages
+ * 1-3): activation outliers are migrated into the weights by a per-channel smoothing, the smoothed
+ * weight W_hat is split by a truncated SVD into a 16-bit low-rank part L1 L2 and a residual
+ * R = W_hat - L1 L2, and both R and the smoothed activation X_hat = X diag(lambda)^-1 are quantized
+ * to 4 bits:
+ *
+ *     Y = X_hat L1 L2 + dequant(Q4(X_hat) Q4(R)) + b
+ *
+ * The engine-design figure of the same README (panels (a), (b)) pairs the steps that share data:
+ * the down projection X_hat L1 shares its input with the activation quantizer
+ * (svdq_quantize_act), and the up projection T L2 shares its output with the 4-bit product
+ * (svdq_linear_w4a4). The Diffusers blog on Nunchaku Lite ("From SVDQuant to Nunchaku Lite" and
+ * its quantization_config example) names the two runtime layer kinds: svdq_w4a4 (attention and
+ * MLP linears, rank-32 low-rank branch) and awq_w4a16 (int4 weights, group 64, 16-bit
+ * activations) for the memory-bound modulation / adaptive-norm projections (awq_linear_w4a16).
+ *
+ * Quantization rule (a fixed reading; the pages do not print one): symmetric INT4, one scale per
+ * group of 64 consecutive inputs along K; scale = float32(absmax) / 7.0f (IEEE division);
+ * code = clamp(round_half_even(x / scale), -8, 7) with an IEEE float32 division; a group whose
+ * scale is 0 (all zeros, or absmax/7 underflows) stores scale 0 and codes 0. For the W4A16
+ * weights the scale is rounded to bfloat16 first and the codes are computed against it.
+ *
+ * Conventions shared by every entry point
+ *   - Return value: SVDQ_OK (0) or a negative SVDQ_ERR_* code; svdq_status_string() names it.
+ *   - Arguments are validated before any HIP call; on an error nothing is enqueued and no output
+ *     is touched.
+ *   - Device entry points take device pointers and a hipStream_t passed as void* (NULL = the
+ *     null stream); they enqueue work and return without synchronising. They allocate nothing,
+ *     keep no pointer after returning and are safe to call from several host threads.
+ *   - The caller owns every buffer. Inputs must stay valid and outputs untouched until the
+ *     enqueued work has completed on the stream.
+ *   - Every pointer must be aligned to 16 bytes. Tensors are dense and row-major.
+ *   - The current device must be a gfx950 (MI355X); otherwise SVDQ_ERR_ARCH.
+ *   - Inputs must be finite (NaN/Inf are outside the contract).
+ *   - Shapes: 1 <= M; K % 64 == 0 and K >= 64; N % 16 == 0 and N >= 16; rank r == 0 or
+ *     r % 16 == 0 with 16 <= r <= 256. All sizes < 2^31 elements per tensor.
+ *
+ * Tensor formats
+ *   bf16        IEEE bfloat16 stored as uint16.
+ *   X           bf16 [M, K].
+ *   inv_smooth  float32 [K]: the reciprocal smoothing factors 1/lambda_k; X_hat = float32(X) * inv
+ *               (one float32 multiply, round to nearest even). NULL means all ones.
+ *   L1t         bf16 [r, K]: L1 transposed.   L2t  bf16 [N, r]: L2 transposed.
+ *   T           bf16 [M, r]: T = bf16( bf16(X_hat) L1 ), float32 accumulation.
+ *   Packed W4A4 codes (activations "qact" [M, K/2] and residual weights "qweight" [N, K/2]):
+ *               byte (row, k/2) holds the code of element k (even) in bits 0-3 and of element
+ *               k+1 in bits 4-7, each as a 4-bit two's-complement integer in [-8, 7]. A weight
+ *               row is one output column n (K contiguous), as in nn.Linear.
+ *   ascale      float32 [K/64, M]: activation scale of (group g, token m) at g*M + m.
+ *   wscale      float32 [K/64, N]: residual-weight scale of (group g, column n) at g*N + n.
+ *   bias        bf16 [N] or NULL.           Y  bf16 [M, N].
+ *   Packed W4A16 weights (awq_linear_w4a16) "qweight": K*N/2 bytes in 512-byte blocks, one per
+ *               (column tile t = n/16, group g), block index t*(K/64) + g. Inside a block, lane
+ *               L = (n % 16) + 16*j (j = 0..3) owns 8 bytes at offset 8*L: two little-endian
+ *               32-bit words h = 0, 1; word h holds the codes of k = 64g + 32h + 8j + s for
+ *               s = 0..7 as offset-binary nibbles (u = code + 8), nibble s at bit offset
+ *               {0, 16, 4, 20, 8, 24, 12, 28}[s].
+ *   W4A16 scales  bf16 [K/64, N].
+ */
+#ifndef SVDQ_H_
+#define SVDQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVDQ_ABI_VERSION 1
+#define SVDQ_GROUP 64
+#define SVDQ_MAX_RANK 256
+
+enum svdq_status {
+  SVDQ_OK = 0,
+  SVDQ_ERR_NULL = -1,    /* a required pointer is NULL, or a pointer is not 16-byte aligned */
+  SVDQ_ERR_SHAPE = -2,   /* a size violates the shape rules above */
+  SVDQ_ERR_RANK = -3,    /* r is not 0 or a multiple of 16 in [16, 256], or r/pointers disagree */
+  SVDQ_ERR_FORMAT = -4,  /* unknown weight format */
+  SVDQ_ERR_ARCH = -5,    /* no HIP device, or the current device is not gfx950 */
+  SVDQ_ERR_LAUNCH = -6   /* the kernel launch failed (hipGetLastError after the launch) */
+};
+
+enum svdq_format {
+  SVDQ_FMT_W4A4_F32SCALE = 0,   /* residual weights for svdq_linear_w4a4, float32 scales */
+  SVDQ_FMT_W4A16_BF16SCALE = 1  /* weights for awq_linear_w4a16, bf16 scales */
+};
+
+/* Name of a status code (static storage; never NULL). */
+const char* svdq_status_string(int status);
+
+/* SVDQ_ABI_VERSION of the built library. */
+int svdq_abi_version(void);
+
+/* SVDQ_OK if the current HIP device is a gfx950, else SVDQ_ERR_ARCH. Caches the answer per
+ * device. The GPU capability check the Diffusers blog describes at load time. */
+int svdq_check_device(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Host-side packing (synchronous, CPU only, no HIP call; caller-owned host buffers).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Bytes of packed codes for a K x N weight: K*N/2 for either format; 0 if the shape is invalid. */
+size_t svdq_packed_weight_bytes(int fmt, int64_t K, int64_t N);
+
+/* Bytes of scales: (K/64)*N*4 for SVDQ_FMT_W4A4_F32SCALE, (K/64)*N*2 for SVDQ_FMT_W4A16_BF16SCALE;
+ * 0 if the shape or format is invalid. */
+size_t svdq_scale_bytes(int fmt, int64_t K, int64_t N);
+
+/* Quantize a float32 weight w [K, N] (row-major, x @ w convention) to INT4 with the rule above,
+ * group 64 along K per column n, and write the packed codes and scales in the format's layout.
+ *   SVDQ_FMT_W4A4_F32SCALE: w is the residual R = W_hat - L1 L2 (overview figure, stage 3);
+ *     qweight_out [N, K/2] bytes, scales_out float32 [K/64, N].
+ *   SVDQ_FMT_W4A16_BF16SCALE: w is the plain weight of an awq_w4a16 projection;
+ *     qweight_out in the W4A16 block layout, scales_out bf16 [K/64, N].
+ * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE (K % 64, N % 16), SVDQ_ERR_FORMAT. */
+int svdq_pack_weights(int fmt, const float* w, int64_t K, int64_t N, uint8_t* qweight_out, void* scales_out);
+
+/* Round the low-rank factors to bf16 and transpose them into the kernels' operand order:
+ * l1 float32 [K, r] -> l1t_out bf16 [r, K]; l2 float32 [r, N] -> l2t_out bf16 [N, r]
+ * (round to nearest even). Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_RANK. */
+int svdq_pack_lowrank(const float* l1, const float* l2, int64_t K, int64_t N, int r,
+                      uint16_t* l1t_out, uint16_t* l2t_out);
+
+/* ---------------------------------------------------------------------------------------------
+ * Device entry points (asynchronous on `stream`).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Fused activation step (engine figure (b): down projection + quantize on one read of X).
+ * Reads X once, forms X_hat = X * inv_smooth, and writes the INT4 codes (qact [M, K/2]), the
+ * per-token group scales (ascale [K/64, M]) and, when r > 0, the 16-bit low-rank activation
+ * T = bf16(bf16(X_hat) L1) (lora_act [M, r]) from l1t [r, K].
+ * r == 0 requires l1t == NULL and lora_act == NULL; r > 0 requires both.
+ * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_RANK, SVDQ_ERR_ARCH, SVDQ_ERR_LAUNCH. */
+int svdq_quantize_act(const void* x, int64_t M, int64_t K, const float* inv_smooth, const void* l1t, int r,
+                      uint8_t* qact, float* ascale, void* lora_act, void* stream);
+
+/* Fused 4-bit product + up projection (engine figure (b)):
+ *   Y = bf16( sum_g ascale[g,m] * wscale[g,n] * P[g,m,n]  +  T L2  +  b )
+ * with P[g,m,n] the exact integer sum over the 64 k of group g of qact code * qweight code.
+ * r == 0 requires lora_act == NULL and l2t == NULL; bias may be NULL.
+ * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_RANK, SVDQ_ERR_ARCH, SVDQ_ERR_LAUNCH. */
+int svdq_linear_w4a4(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                     const void* lora_act, const void* l2t, int r, const void* bias, void* y,
+                     int64_t M, int64_t N, int64_t K, void* stream);
+
+/* W4A16 projection (awq_w4a16 layers of the Diffusers blog): Y = bf16( X dequant(qweight, scales) + b ),
+ * X bf16 [M, K], packed weights in the W4A16 block layout, scales bf16 [K/64, N], bias bf16 [N] or NULL.
+ * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_ARCH, SVDQ_ERR_LAUNCH. */
+int awq_linear_w4a16(const void* x, const uint8_t* qweight, const void* scales, const void* bias, void* y,
+                     int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Parity/debug export of the exact per-group integer sums of the W4A4 product for the window
+ * rows [m0, m0+tm) x columns [n0, n0+tn): out int32 [K/64, tm, tn] (out[(g*tm + i)*tn + j] =
+ * P[g, m0+i, n0+j]). Uses the same kernel as svdq_linear_w4a4 with its epilogue replaced.
+ * Requires 0 <= m0, m0 + tm <= M, 0 <= n0, n0 + tn <= N, tm >= 1, tn >= 1.
+ * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_ARCH, SVDQ_ERR_LAUNCH. */
+int svdq_debug_group_sums(const uint8_t* qact, const uint8_t* qweight, int64_t M, int64_t N, int64_t K,
+                          int64_t m0, int64_t n0, int64_t tm, int64_t tn, int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H_ */

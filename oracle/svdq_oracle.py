@@ -87,17 +87,19 @@ def smoothing_factors(x: np.ndarray, w: np.ndarray):
     return inv, lam_prime
 
 
-def svdq_decompose(x: np.ndarray, w: np.ndarray, rank: int):
+def svdq_decompose(x: np.ndarray, w: np.ndarray, rank: int, svd=None):
     """Smoothing + truncated SVD + residual (stages 2-3 of the SVDQuant overview figure).
 
     x: float32 [M, K] activations used for calibration; w: float32 [K, N] weights (x @ w).
     W_hat = diag(lambda') w; W_hat = U S V^T; L1 = U_r S_r, L2 = V_r^T (float64).
     The runtime factors are bf16(L1), bf16(L2); the residual that gets quantized is
     R = W_hat - bf16(L1) bf16(L2), computed in float64 and stored as float32.
+    ``svd`` may pass in numpy.linalg.svd(W_hat, full_matrices=False) of this same W_hat, so that
+    several ranks of one layer share one factorisation.
     """
     inv, lam_prime = smoothing_factors(x, w)
     w_hat = lam_prime[:, None] * w.astype(np.float64)
-    u, s, vt = np.linalg.svd(w_hat, full_matrices=False)
+    u, s, vt = np.linalg.svd(w_hat, full_matrices=False) if svd is None else svd
     l1 = u[:, :rank] * s[:rank]
     l2 = vt[:rank, :]
     l1_b = bf16_round(l1.astype(np.float32))

@@ -1,0 +1,233 @@
+"""Thin ctypes binding of ``libsvdq.so`` (the C ABI in include/svdq.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP kernels (device
+entry points) or its C++ packer (host entry points). Functions carry the C names; device entry
+points take torch tensors on the current HIP device and enqueue on the current torch stream
+unless a stream handle is given. There is no fallback: a missing library or a non-gfx950 device
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsvdq.so")
+_lib = None
+
+SVDQ_OK = 0
+SVDQ_FMT_W4A4_F32SCALE = 0
+SVDQ_FMT_W4A16_BF16SCALE = 1
+GROUP = 64
+
+_vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+_SIGNATURES = {
+    "svdq_status_string": (ctypes.c_char_p, [_int]),
+    "svdq_abi_version": (_int, []),
+    "svdq_check_device": (_int, []),
+    "svdq_packed_weight_bytes": (_sz, [_int, _i64, _i64]),
+    "svdq_scale_bytes": (_sz, [_int, _i64, _i64]),
+    "svdq_pack_weights": (_int, [_int, _vp, _i64, _i64, _vp, _vp]),
+    "svdq_pack_lowrank": (_int, [_vp, _vp, _i64, _i64, _int, _vp, _vp]),
+    "svdq_quantize_act": (_int, [_vp, _i64, _i64, _vp, _vp, _int, _vp, _vp, _vp, _vp]),
+    "svdq_linear_w4a4": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "awq_linear_w4a16": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "svdq_debug_group_sums": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp]),
+}
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {_LIB_PATH} is missing "
+                               "(run quantized_gemm_amd/build.py or __graft_entry__.build())")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().svdq_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SVDQ_OK:
+        raise SvdqError(fn, status)
+
+
+def svdq_abi_version() -> int:
+    return load_library().svdq_abi_version()
+
+
+def svdq_check_device() -> None:
+    _check("svdq_check_device", load_library().svdq_check_device())
+
+
+# ------------------------------------------------------------------------------------------------
+# Host packer (numpy in, numpy out)
+# ------------------------------------------------------------------------------------------------
+def _np_ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _aligned_empty(nbytes: int, dtype) -> np.ndarray:
+    raw = np.empty(nbytes + 64, dtype=np.uint8)
+    off = (-raw.ctypes.data) % 64
+    return raw[off:off + nbytes].view(dtype)
+
+
+def svdq_pack_weights(fmt: int, w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Pack a float32 [K, N] weight; returns (qweight uint8 [K*N/2], scales [K/64, N])."""
+    lib = load_library()
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    K, N = w.shape
+    qbytes = lib.svdq_packed_weight_bytes(fmt, K, N)
+    sbytes = lib.svdq_scale_bytes(fmt, K, N)
+    if qbytes == 0 or sbytes == 0:
+        _check("svdq_pack_weights", lib.svdq_pack_weights(fmt, None, K, N, None, None) or -2)
+    q = _aligned_empty(qbytes, np.uint8)
+    s = _aligned_empty(sbytes, np.float32 if fmt == SVDQ_FMT_W4A4_F32SCALE else np.uint16)
+    _check("svdq_pack_weights", lib.svdq_pack_weights(fmt, _np_ptr(w), K, N, _np_ptr(q), _np_ptr(s)))
+    return q, s.reshape(K // GROUP, N)
+
+
+def svdq_pack_lowrank(l1: np.ndarray, l2: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """float32 L1 [K, r], L2 [r, N] -> bf16 bits L1^T [r, K], L2^T [N, r]."""
+    l1 = np.ascontiguousarray(l1, dtype=np.float32)
+    l2 = np.ascontiguousarray(l2, dtype=np.float32)
+    K, r = l1.shape
+    r2, N = l2.shape
+    if r2 != r:
+        raise ValueError("L1 [K, r] and L2 [r, N] disagree on r")
+    l1t = _aligned_empty(r * K * 2, np.uint16).reshape(r, K)
+    l2t = _aligned_empty(N * r * 2, np.uint16).reshape(N, r)
+    _check("svdq_pack_lowrank", load_library().svdq_pack_lowrank(_np_ptr(l1), _np_ptr(l2), K, N, r,
+                                                                 _np_ptr(l1t), _np_ptr(l2t)))
+    return l1t, l2t
+
+
+# ------------------------------------------------------------------------------------------------
+# Device entry points (torch tensors on the current HIP device)
+# ------------------------------------------------------------------------------------------------
+def _dev_ptr(t, name: str, dtypes, shape=None) -> int:
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _bf16():
+    import torch
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def svdq_quantize_act(x, inv_smooth, l1t, qact=None, ascale=None, lora_act=None, stream=None):
+    """Kernel (a). x bf16 [M, K]; inv_smooth float32 [K] or None; l1t bf16 [r, K] or None.
+
+    Returns (qact uint8 [M, K/2], ascale float32 [K/64, M], lora_act bf16 [M, r] or None).
+    """
+    import torch
+    M, K = x.shape
+    r = 0 if l1t is None else l1t.shape[0]
+    dev = x.device
+    if qact is None:
+        qact = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if ascale is None:
+        ascale = torch.empty((K // GROUP, M), dtype=torch.float32, device=dev)
+    if r and lora_act is None:
+        lora_act = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    st = load_library().svdq_quantize_act(
+        _dev_ptr(x, "x", _bf16()), M, K, _dev_ptr(inv_smooth, "inv_smooth", (torch.float32,), (K,)),
+        _dev_ptr(l1t, "l1t", _bf16(), (r, K) if r else None), r,
+        _dev_ptr(qact, "qact", (torch.uint8,), (M, K // 2)), _dev_ptr(ascale, "ascale", (torch.float32,), (K // GROUP, M)),
+        _dev_ptr(lora_act, "lora_act", _bf16(), (M, r)) if r else None, _stream(stream))
+    _check("svdq_quantize_act", st)
+    return qact, ascale, (lora_act if r else None)
+
+
+def svdq_linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, bias, y=None, stream=None):
+    """Kernel (b). Returns y bf16 [M, N]."""
+    import torch
+    M, KB = qact.shape
+    K = 2 * KB
+    N = wscale.shape[1]
+    r = 0 if l2t is None else l2t.shape[1]
+    if qweight.numel() != N * K // 2:
+        raise ValueError("qweight size does not match [N, K/2]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=qact.device)
+    st = load_library().svdq_linear_w4a4(
+        _dev_ptr(qact, "qact", (torch.uint8,)), _dev_ptr(ascale, "ascale", (torch.float32,), (K // GROUP, M)),
+        _dev_ptr(qweight, "qweight", (torch.uint8,)), _dev_ptr(wscale, "wscale", (torch.float32,), (K // GROUP, N)),
+        _dev_ptr(lora_act, "lora_act", _bf16(), (M, r)) if r else None,
+        _dev_ptr(l2t, "l2t", _bf16(), (N, r)) if r else None, r,
+        _dev_ptr(bias, "bias", _bf16(), (N,)), _dev_ptr(y, "y", _bf16(), (M, N)), M, N, K, _stream(stream))
+    _check("svdq_linear_w4a4", st)
+    return y
+
+
+def awq_linear_w4a16(x, qweight, scales, bias, y=None, stream=None):
+    """Kernel (c). x bf16 [M, K]; qweight uint8 (W4A16 block layout); scales bf16 [K/64, N]."""
+    import torch
+    M, K = x.shape
+    N = scales.shape[1]
+    if qweight.numel() != N * K // 2:
+        raise ValueError("qweight size does not match K*N/2")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    st = load_library().awq_linear_w4a16(
+        _dev_ptr(x, "x", _bf16()), _dev_ptr(qweight, "qweight", (torch.uint8,)),
+        _dev_ptr(scales, "scales", _bf16(), (K // GROUP, N)), _dev_ptr(bias, "bias", _bf16(), (N,)),
+        _dev_ptr(y, "y", _bf16(), (M, N)), M, N, K, _stream(stream))
+    _check("awq_linear_w4a16", st)
+    return y
+
+
+def svdq_debug_group_sums(qact, qweight, N: int, m0: int, n0: int, tm: int, tn: int, out=None, stream=None):
+    """Exact per-group integer sums P[g, m0+i, n0+j] of the W4A4 product: int32 [K/64, tm, tn]."""
+    import torch
+    M, KB = qact.shape
+    K = 2 * KB
+    if out is None:
+        out = torch.empty((K // GROUP, tm, tn), dtype=torch.int32, device=qact.device)
+    st = load_library().svdq_debug_group_sums(
+        _dev_ptr(qact, "qact", (torch.uint8,)), _dev_ptr(qweight, "qweight", (torch.uint8,)), M, N, K, m0, n0, tm, tn,
+        _dev_ptr(out, "out", (torch.int32,), (K // GROUP, tm, tn)), _stream(stream))
+    _check("svdq_debug_group_sums", st)
+    return out

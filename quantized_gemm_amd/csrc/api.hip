@@ -1,0 +1,133 @@
+// C ABI of the library (see include/svdq.h): argument validation, the gfx950 device check and
+// the kernel launches. Validation happens before any HIP call; on an error nothing is enqueued.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/svdq.h"
+#include "svdq_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch_state[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool mk_ok(int64_t M, int64_t K) {
+  return M >= 1 && M < (int64_t(1) << 31) && K >= SVDQ_GROUP && K % SVDQ_GROUP == 0 && K < (int64_t(1) << 31) &&
+         M * K < (int64_t(1) << 40);
+}
+
+bool n_ok(int64_t N) { return N >= 16 && N % 16 == 0 && N < (int64_t(1) << 31); }
+
+bool rank_ok(int r) { return r == 0 || (r >= 16 && r <= SVDQ_MAX_RANK && r % 16 == 0); }
+
+int device_status() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return SVDQ_ERR_ARCH;
+  }
+  if (dev < kMaxDevices) {
+    const int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 1) return SVDQ_OK;
+    if (st == 2) return SVDQ_ERR_ARCH;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return SVDQ_ERR_ARCH;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? SVDQ_OK : SVDQ_ERR_ARCH;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* svdq_status_string(int status) {
+  switch (status) {
+    case SVDQ_OK: return "SVDQ_OK";
+    case SVDQ_ERR_NULL: return "SVDQ_ERR_NULL: a required pointer is NULL or not 16-byte aligned";
+    case SVDQ_ERR_SHAPE: return "SVDQ_ERR_SHAPE: sizes violate M>=1, K%64==0, N%16==0";
+    case SVDQ_ERR_RANK: return "SVDQ_ERR_RANK: rank must be 0 or a multiple of 16 in [16, 256], matching the pointers";
+    case SVDQ_ERR_FORMAT: return "SVDQ_ERR_FORMAT: unknown weight format";
+    case SVDQ_ERR_ARCH: return "SVDQ_ERR_ARCH: no HIP device, or the current device is not gfx950";
+    case SVDQ_ERR_LAUNCH: return "SVDQ_ERR_LAUNCH: kernel launch failed";
+    default: return "SVDQ_ERR_UNKNOWN";
+  }
+}
+
+int svdq_abi_version(void) { return SVDQ_ABI_VERSION; }
+
+int svdq_check_device(void) { return device_status(); }
+
+int svdq_quantize_act(const void* x, int64_t M, int64_t K, const float* inv_smooth, const void* l1t, int r,
+                      uint8_t* qact, float* ascale, void* lora_act, void* stream) {
+  if (x == nullptr || qact == nullptr || ascale == nullptr) return SVDQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(qact) || !aligned16(ascale) || (inv_smooth && !aligned16(inv_smooth)) ||
+      (l1t && !aligned16(l1t)) || (lora_act && !aligned16(lora_act)))
+    return SVDQ_ERR_NULL;
+  if (!mk_ok(M, K)) return SVDQ_ERR_SHAPE;
+  if (!rank_ok(r)) return SVDQ_ERR_RANK;
+  if ((r == 0) != (l1t == nullptr) || (r == 0) != (lora_act == nullptr)) return SVDQ_ERR_RANK;
+  const int st = device_status();
+  if (st != SVDQ_OK) return st;
+  return launch_status(svdq::launch_quantize_act(static_cast<const uint16_t*>(x), (int)M, (int)K, inv_smooth,
+                                                 static_cast<const uint16_t*>(l1t), r, qact, ascale,
+                                                 static_cast<uint16_t*>(lora_act),
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int svdq_linear_w4a4(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                     const void* lora_act, const void* l2t, int r, const void* bias, void* y, int64_t M, int64_t N,
+                     int64_t K, void* stream) {
+  if (qact == nullptr || ascale == nullptr || qweight == nullptr || wscale == nullptr || y == nullptr)
+    return SVDQ_ERR_NULL;
+  if (!aligned16(qact) || !aligned16(ascale) || !aligned16(qweight) || !aligned16(wscale) || !aligned16(y) ||
+      (lora_act && !aligned16(lora_act)) || (l2t && !aligned16(l2t)) || (bias && !aligned16(bias)))
+    return SVDQ_ERR_NULL;
+  if (!mk_ok(M, K) || !n_ok(N) || N * K >= (int64_t(1) << 40) || M * N >= (int64_t(1) << 40)) return SVDQ_ERR_SHAPE;
+  if (!rank_ok(r)) return SVDQ_ERR_RANK;
+  if ((r == 0) != (lora_act == nullptr) || (r == 0) != (l2t == nullptr)) return SVDQ_ERR_RANK;
+  const int st = device_status();
+  if (st != SVDQ_OK) return st;
+  return launch_status(svdq::launch_w4a4_gemm(qact, ascale, qweight, wscale, static_cast<const uint16_t*>(lora_act),
+                                              static_cast<const uint16_t*>(l2t), r,
+                                              static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), (int)M,
+                                              (int)N, (int)K, static_cast<hipStream_t>(stream)));
+}
+
+int awq_linear_w4a16(const void* x, const uint8_t* qweight, const void* scales, const void* bias, void* y, int64_t M,
+                     int64_t N, int64_t K, void* stream) {
+  if (x == nullptr || qweight == nullptr || scales == nullptr || y == nullptr) return SVDQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y) || (bias && !aligned16(bias)))
+    return SVDQ_ERR_NULL;
+  if (!mk_ok(M, K) || !n_ok(N) || N * K >= (int64_t(1) << 40) || M * N >= (int64_t(1) << 40)) return SVDQ_ERR_SHAPE;
+  const int st = device_status();
+  if (st != SVDQ_OK) return st;
+  return launch_status(svdq::launch_w4a16(static_cast<const uint16_t*>(x), qweight,
+                                          static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(bias),
+                                          static_cast<uint16_t*>(y), (int)M, (int)N, (int)K,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int svdq_debug_group_sums(const uint8_t* qact, const uint8_t* qweight, int64_t M, int64_t N, int64_t K, int64_t m0,
+                          int64_t n0, int64_t tm, int64_t tn, int32_t* out, void* stream) {
+  if (qact == nullptr || qweight == nullptr || out == nullptr) return SVDQ_ERR_NULL;
+  if (!aligned16(qact) || !aligned16(qweight) || !aligned16(out)) return SVDQ_ERR_NULL;
+  if (!mk_ok(M, K) || !n_ok(N)) return SVDQ_ERR_SHAPE;
+  if (m0 < 0 || n0 < 0 || tm < 1 || tn < 1 || m0 + tm > M || n0 + tn > N) return SVDQ_ERR_SHAPE;
+  if ((K / SVDQ_GROUP) * tm * tn >= (int64_t(1) << 31)) return SVDQ_ERR_SHAPE;
+  const int st = device_status();
+  if (st != SVDQ_OK) return st;
+  return launch_status(svdq::launch_w4a4_group_sums(qact, qweight, (int)M, (int)N, (int)K, (int)m0, (int)n0, (int)tm,
+                                                    (int)tn, out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

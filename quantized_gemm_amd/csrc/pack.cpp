@@ -1,0 +1,169 @@
+// Host-side weight packing (CPU, synchronous): INT4 quantization of the residual / W4A16 weights
+// and the bf16 transposes of the low-rank factors, in the layouts documented in include/svdq.h.
+//
+// The residual R = W_hat - L1 L2 of the SVDQuant overview figure (Nunchaku README, "Method >
+// Quantization method - SVDQuant", stage 3) is quantized per output column along K in groups of
+// 64 (scale = absmax / 7 in float32, IEEE division; code = clamp(round_half_even(w / scale), -8, 7)).
+// The W4A16 weights (the awq_w4a16 layers of the Diffusers blog on Nunchaku Lite: int4, group 64)
+// use a bf16 scale, rounded first; their codes are taken against the rounded scale.
+//
+// Floating-point determinism: the file is built without fast-math and without contraction, and
+// the routines run with the SSE flush-to-zero / denormals-are-zero bits cleared, so subnormal
+// weights and scales follow IEEE semantics whatever the calling process configured.
+#include <xmmintrin.h>
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "../../include/svdq.h"
+
+namespace {
+
+class IeeeDenormalGuard {
+ public:
+  IeeeDenormalGuard() : saved_(_mm_getcsr()) { _mm_setcsr(saved_ & ~(0x8040u)); }  // clear FTZ (15), DAZ (6)
+  ~IeeeDenormalGuard() { _mm_setcsr(saved_); }
+
+ private:
+  unsigned saved_;
+};
+
+inline uint16_t bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+inline float bf16_value(uint16_t h) {
+  const uint32_t u = static_cast<uint32_t>(h) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// The INT4 rule for one value against a non-zero scale.
+inline int int4_code(float v, float s) {
+  volatile float q = v / s;  // one IEEE float32 division, rounded to nearest
+  float c = std::nearbyint(static_cast<float>(q));  // ties to even in the default rounding mode
+  if (c < -8.0f) c = -8.0f;
+  if (c > 7.0f) c = 7.0f;
+  return static_cast<int>(c);
+}
+
+bool shape_ok(int64_t K, int64_t N) {
+  return K >= SVDQ_GROUP && K % SVDQ_GROUP == 0 && N >= 16 && N % 16 == 0 && K < (int64_t(1) << 31) &&
+         N < (int64_t(1) << 31) && K * N < (int64_t(1) << 40);
+}
+
+// Per (group g, column n) absmax of w [K, N], scanning rows contiguously.
+void group_absmax(const float* w, int64_t K, int64_t N, std::vector<float>& amax) {
+  const int64_t G = K / SVDQ_GROUP;
+  amax.assign(static_cast<size_t>(G * N), 0.0f);
+  for (int64_t k = 0; k < K; ++k) {
+    float* am = amax.data() + (k / SVDQ_GROUP) * N;
+    const float* row = w + k * N;
+    for (int64_t n = 0; n < N; ++n) {
+      const float a = std::fabs(row[n]);
+      if (a > am[n]) am[n] = a;
+    }
+  }
+}
+
+void pack_w4a4(const float* w, int64_t K, int64_t N, uint8_t* q, float* scales) {
+  std::vector<float> amax;
+  group_absmax(w, K, N, amax);
+  const int64_t G = K / SVDQ_GROUP;
+  for (int64_t i = 0; i < G * N; ++i) {
+    volatile float s = amax[static_cast<size_t>(i)] / 7.0f;
+    scales[i] = s;
+  }
+  std::memset(q, 0, static_cast<size_t>(K * N / 2));
+  const int64_t KB = K / 2;
+  for (int64_t k = 0; k < K; ++k) {
+    const float* row = w + k * N;
+    const float* srow = scales + (k / SVDQ_GROUP) * N;
+    const int shift = (k & 1) ? 4 : 0;
+    for (int64_t n = 0; n < N; ++n) {
+      const float s = srow[n];
+      const int c = (s == 0.0f) ? 0 : int4_code(row[n], s);
+      q[n * KB + k / 2] |= static_cast<uint8_t>((c & 0xF) << shift);
+    }
+  }
+}
+
+// Nibble bit offset of slot s (0..7) inside a 32-bit word of the W4A16 block layout.
+constexpr int kW4A16NibbleShift[8] = {0, 16, 4, 20, 8, 24, 12, 28};
+
+void pack_w4a16(const float* w, int64_t K, int64_t N, uint8_t* q, uint16_t* scales) {
+  std::vector<float> amax;
+  group_absmax(w, K, N, amax);
+  const int64_t G = K / SVDQ_GROUP;
+  std::vector<float> sval(static_cast<size_t>(G * N));
+  for (int64_t i = 0; i < G * N; ++i) {
+    volatile float s = amax[static_cast<size_t>(i)] / 7.0f;
+    scales[i] = bf16_rne(s);
+    sval[static_cast<size_t>(i)] = bf16_value(scales[i]);
+  }
+  std::memset(q, 0, static_cast<size_t>(K * N / 2));
+  for (int64_t k = 0; k < K; ++k) {
+    const int64_t g = k / SVDQ_GROUP;
+    const int64_t kk = k % SVDQ_GROUP;        // 32h + 8j + s
+    const int64_t h = kk / 32, jj = (kk % 32) / 8, s = kk % 8;
+    const float* row = w + k * N;
+    for (int64_t n = 0; n < N; ++n) {
+      const float sc = sval[static_cast<size_t>(g * N + n)];
+      const int c = (sc == 0.0f) ? 0 : int4_code(row[n], sc);
+      const uint32_t u = static_cast<uint32_t>(c + 8) & 0xFu;
+      const int64_t t = n / 16, lane = (n % 16) + 16 * jj;
+      const int64_t word = ((t * G + g) * 64 + lane) * 2 + h;
+      uint32_t* wp = reinterpret_cast<uint32_t*>(q) + word;
+      *wp |= u << kW4A16NibbleShift[s];
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t svdq_packed_weight_bytes(int fmt, int64_t K, int64_t N) {
+  if (fmt != SVDQ_FMT_W4A4_F32SCALE && fmt != SVDQ_FMT_W4A16_BF16SCALE) return 0;
+  if (!shape_ok(K, N)) return 0;
+  return static_cast<size_t>(K * N / 2);
+}
+
+size_t svdq_scale_bytes(int fmt, int64_t K, int64_t N) {
+  if (!shape_ok(K, N)) return 0;
+  if (fmt == SVDQ_FMT_W4A4_F32SCALE) return static_cast<size_t>((K / SVDQ_GROUP) * N * 4);
+  if (fmt == SVDQ_FMT_W4A16_BF16SCALE) return static_cast<size_t>((K / SVDQ_GROUP) * N * 2);
+  return 0;
+}
+
+int svdq_pack_weights(int fmt, const float* w, int64_t K, int64_t N, uint8_t* qweight_out, void* scales_out) {
+  if (fmt != SVDQ_FMT_W4A4_F32SCALE && fmt != SVDQ_FMT_W4A16_BF16SCALE) return SVDQ_ERR_FORMAT;
+  if (w == nullptr || qweight_out == nullptr || scales_out == nullptr) return SVDQ_ERR_NULL;
+  if (!shape_ok(K, N)) return SVDQ_ERR_SHAPE;
+  IeeeDenormalGuard guard;
+  if (fmt == SVDQ_FMT_W4A4_F32SCALE)
+    pack_w4a4(w, K, N, qweight_out, static_cast<float*>(scales_out));
+  else
+    pack_w4a16(w, K, N, qweight_out, static_cast<uint16_t*>(scales_out));
+  return SVDQ_OK;
+}
+
+int svdq_pack_lowrank(const float* l1, const float* l2, int64_t K, int64_t N, int r, uint16_t* l1t_out,
+                      uint16_t* l2t_out) {
+  if (l1 == nullptr || l2 == nullptr || l1t_out == nullptr || l2t_out == nullptr) return SVDQ_ERR_NULL;
+  if (!shape_ok(K, N)) return SVDQ_ERR_SHAPE;
+  if (r < 16 || r > SVDQ_MAX_RANK || r % 16 != 0) return SVDQ_ERR_RANK;
+  IeeeDenormalGuard guard;
+  for (int64_t k = 0; k < K; ++k)
+    for (int j = 0; j < r; ++j) l1t_out[static_cast<int64_t>(j) * K + k] = bf16_rne(l1[k * r + j]);
+  for (int j = 0; j < r; ++j)
+    for (int64_t n = 0; n < N; ++n) l2t_out[n * r + j] = bf16_rne(l2[static_cast<int64_t>(j) * N + n]);
+  return SVDQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+"""Shared test fixtures: synthetic layer problems prepared and evaluated by the oracle, plus the
+independent decoders / encoders of the packed layouts documented in include/svdq.h.
+
+Only the oracle produces expected values here; the GPU path's outputs are compared against them.
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+import oracle
+import synth
+
+
+@functools.lru_cache(maxsize=2)
+def _raw(name: str, M: int):
+    """Drawn inputs and the SVD of the smoothed weight, shared by every rank of one layer."""
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_layer_inputs(cfg, M=M)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    _, lam_prime = oracle.smoothing_factors(x, w)
+    svd = np.linalg.svd(lam_prime[:, None] * w.astype(np.float64), full_matrices=False)
+    return inp, x, w, svd
+
+
+@functools.lru_cache(maxsize=3)
+def w4a4_problem(name: str, M: int = None, rank: int = None):
+    """Inputs + oracle results for one W4A4 configuration (optionally with another M or rank)."""
+    cfg = synth.CONFIGS[name]
+    if rank is not None:
+        cfg = cfg.with_rank(rank)
+    inp, x, w, svd = _raw(name, M)
+    b = synth.f32_from_bf16_bits(inp["bias"]) if inp["bias"] is not None else None
+    d = oracle.svdq_decompose(x, w, cfg.rank, svd=svd)
+    out = oracle.svdq_layer(x, d["inv"], d["l1_bf16"], d["l2_bf16"], d["resid"], b)
+    return {"cfg": cfg, "x_bits": inp["x"], "x": x, "bias_bits": inp["bias"], "bias": b,
+            "inv": d["inv"], "l1": d["l1_bf16"], "l2": d["l2_bf16"], "resid": d["resid"], **out}
+
+
+@functools.lru_cache(maxsize=4)
+def w4a16_problem(name: str = "awq", M: int = None, with_bias: bool = False):
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_layer_inputs(cfg, M=M)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    b = None
+    if with_bias:
+        b = oracle.bf16_round(synth.random_f32((cfg.N,), seed=cfg.seed + 100, scale=0.01))
+    codes, s = oracle.quantize_weights_w4a16(w)
+    y64, y = oracle.awq_linear(x, codes, s, b)
+    return {"cfg": cfg, "x_bits": inp["x"], "x": x, "w": w, "bias": b, "codes": codes, "scales": s,
+            "y64": y64, "y": y}
+
+
+def decode_qact(packed: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """[rows, K/2] bytes (low nibble = even k, two's complement) -> int8 [rows, K]."""
+    b = np.asarray(packed, dtype=np.uint8).reshape(rows, K // 2).astype(np.int16)
+    out = np.empty((rows, K), np.int16)
+    out[:, 0::2] = b & 0xF
+    out[:, 1::2] = (b >> 4) & 0xF
+    out[out >= 8] -= 16
+    return out.astype(np.int8)
+
+
+def bf16_bits(a_f32: np.ndarray) -> np.ndarray:
+    return synth.bf16_bits_from_f32(a_f32)
+
+
+def tolerance_report(y: np.ndarray, y_ref: np.ndarray):
+    """(max|err| / max|Y_ref|, sum|err| / sum|Y_ref|) in float64."""
+    y = y.astype(np.float64)
+    y_ref = y_ref.astype(np.float64)
+    err = np.abs(y - y_ref)
+    return float(err.max() / np.abs(y_ref).max()), float(err.sum() / np.abs(y_ref).sum())
+
+
+def within_one_bf16_ulp(a: np.ndarray, b: np.ndarray, abs_floor: float) -> np.ndarray:
+    """Elementwise: bf16 values a and b are equal, adjacent, or both within abs_floor of each other."""
+    ab = synth.bf16_bits_from_f32(a).astype(np.int32)
+    bb = synth.bf16_bits_from_f32(b).astype(np.int32)
+    same_sign = (ab >> 15) == (bb >> 15)
+    adjacent = same_sign & (np.abs(ab - bb) <= 1)
+    return adjacent | (np.abs(a.astype(np.float64) - b.astype(np.float64)) <= abs_floor)

@@ -1,0 +1,263 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI (needs an MI355X).
+
+Bar: INT4 codes, scales and per-group integer sums bit-exact; T within one bf16 ulp;
+Y (bf16) with max|err| <= 1e-2 * max|Y_ref| and sum|err| / sum|Y_ref| <= 2e-3.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from problems import (decode_qact, tolerance_report, w4a16_problem, w4a4_problem, within_one_bf16_ulp)
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 1e-2
+MEAN_REL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    import quantized_gemm_amd as q
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    q.load_library()
+    q.svdq_check_device()
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_bf16(bits: np.ndarray, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def to_dev(a: np.ndarray, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def bf16_to_np(t) -> np.ndarray:
+    import torch
+    return synth.f32_from_bf16_bits(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+class Layer:
+    """The packed layer on the device (weights packed by the library's host packer)."""
+
+    def __init__(self, p, dev, resid=None):
+        import quantized_gemm_amd as q
+        cfg = p["cfg"]
+        self.r = cfg.rank
+        qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, p["resid"] if resid is None else resid)
+        self.qw, self.sw = to_dev(qw, dev), to_dev(sw, dev)
+        self.inv = to_dev(p["inv"], dev)
+        if self.r:
+            l1t, l2t = q.svdq_pack_lowrank(p["l1"], p["l2"])
+            self.l1t, self.l2t = to_dev_bf16(l1t, dev), to_dev_bf16(l2t, dev)
+        else:
+            self.l1t = self.l2t = None
+        self.bias = None if p["bias_bits"] is None else to_dev_bf16(p["bias_bits"], dev)
+
+    def run(self, x_bits, dev):
+        import torch
+        import quantized_gemm_amd as q
+        x = to_dev_bf16(x_bits, dev)
+        qact, ascale, t = q.svdq_quantize_act(x, self.inv, self.l1t)
+        y = q.svdq_linear_w4a4(qact, ascale, self.qw, self.sw, t, self.l2t, self.bias)
+        torch.cuda.synchronize()
+        return qact, ascale, t, y
+
+
+def check_activation_outputs(p, qact, ascale, t, rows=None):
+    M, K = p["x"].shape if rows is None else (rows, p["x"].shape[1])
+    codes = decode_qact(qact.cpu().numpy(), M, K)
+    assert np.array_equal(codes, p["qa"][:M]), "INT4 activation codes differ"
+    sa = ascale.cpu().numpy()
+    assert np.array_equal(sa.view(np.uint32), np.ascontiguousarray(p["sa"][:, :M]).view(np.uint32)), \
+        "activation scales differ"
+    if p["cfg"].rank:
+        tg = bf16_to_np(t)
+        tr = p["t"][:M]
+        ok = within_one_bf16_ulp(tg, tr, abs_floor=2.0 ** -16 * float(np.abs(tr).max()))
+        assert ok.all(), f"T beyond one bf16 ulp at {np.argwhere(~ok)[:5]}"
+        say(f"  T exact fraction {np.mean(tg == tr):.6f}")
+
+
+def check_y(p, y, rows=None):
+    yr = p["y"] if rows is None else p["y"][:rows]
+    yg = bf16_to_np(y)
+    mx, mean = tolerance_report(yg, yr)
+    say(f"  Y max|err|/max|Y| = {mx:.3e}, mean rel = {mean:.3e}")
+    assert mx <= MAX_REL and mean <= MEAN_REL
+
+
+# ---------------------------------------------------------------------------------------------
+# whole-layer parity on every W4A4 configuration
+# ---------------------------------------------------------------------------------------------
+W4A4_CASES = [("tiny", None), ("attn", None), ("up", None), ("down", None),
+              ("qkv_r32", 32), ("qkv_r32", 128), ("qkv_r32", 256)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,rank", W4A4_CASES, ids=[f"{n}-r{r or ''}" for n, r in W4A4_CASES])
+def test_w4a4_layer_parity(gpu, name, rank):
+    import quantized_gemm_amd as q
+    say(f"[w4a4 parity] {name} rank={rank}: building oracle problem")
+    p = w4a4_problem(name, rank=rank)
+    cfg = p["cfg"]
+    M, K = p["x"].shape
+    N = p["resid"].shape[1]
+    say(f"[w4a4 parity] {cfg.name} M={M} K={K} N={N} r={cfg.rank}: running GPU")
+    layer = Layer(p, gpu)
+    qact, ascale, t, y = layer.run(p["x_bits"], gpu)
+    check_activation_outputs(p, qact, ascale, t)
+    check_y(p, y)
+    # exact per-group integer sums on windows: the corner, the ragged far corner, the middle
+    wins = [(0, 0, min(M, 64), min(N, 64)), (M - 37, N - 53, 37, 53), (M // 2 - 20, N // 2 - 24, 40, 48)]
+    for (m0, n0, tm, tn) in wins:
+        got = q.svdq_debug_group_sums(qact, layer.qw, N, m0, n0, tm, tn).cpu().numpy()
+        ref = oracle.group_sums(p["qa"][m0:m0 + tm], p["qw"][:, n0:n0 + tn])
+        assert np.array_equal(got, ref), f"group sums differ in window {(m0, n0, tm, tn)}"
+    # run-to-run determinism (no atomics, fixed reduction order)
+    qact2, ascale2, t2, y2 = layer.run(p["x_bits"], gpu)
+    import torch
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert np.array_equal(qact.cpu().numpy(), qact2.cpu().numpy())
+
+
+def test_tiny_full_group_sums(gpu):
+    import quantized_gemm_amd as q
+    p = w4a4_problem("tiny")
+    layer = Layer(p, gpu)
+    qact, _, _, _ = layer.run(p["x_bits"], gpu)
+    M, K = p["x"].shape
+    N = p["resid"].shape[1]
+    got = q.svdq_debug_group_sums(qact, layer.qw, N, 0, 0, M, N).cpu().numpy()
+    assert np.array_equal(got, oracle.group_sums(p["qa"], p["qw"]))
+
+
+@pytest.mark.parametrize("rows", [1, 7, 16, 17, 100, 129, 255])
+def test_ragged_token_counts(gpu, rows):
+    """Rows are independent: a prefix of the tokens gives the prefix of every output."""
+    p = w4a4_problem("tiny")
+    layer = Layer(p, gpu)
+    qact, ascale, t, y = layer.run(p["x_bits"][:rows], gpu)
+    check_activation_outputs(p, qact, ascale, t, rows=rows)
+    check_y(p, y, rows=rows)
+
+
+def test_rank_zero(gpu):
+    p = w4a4_problem("tiny", rank=0)
+    assert p["t"] is None
+    layer = Layer(p, gpu)
+    qact, ascale, t, y = layer.run(p["x_bits"], gpu)
+    assert t is None
+    check_activation_outputs(p, qact, ascale, t)
+    check_y(p, y)
+
+
+def test_zero_residual_gives_lowrank_plus_bias(gpu):
+    p = w4a4_problem("tiny")
+    zero = np.zeros_like(p["resid"])
+    ref = oracle.svdq_layer(p["x"], p["inv"], p["l1"], p["l2"], zero, p["bias"])
+    layer = Layer(p, gpu, resid=zero)
+    _, _, _, y = layer.run(p["x_bits"], gpu)
+    mx, mean = tolerance_report(bf16_to_np(y), ref["y"])
+    assert mx <= MAX_REL and mean <= MEAN_REL
+
+
+def test_column_slice_invariance(gpu):
+    """Output columns are independent (fused Q|K|V slices): an N-slice of the packed weights gives
+    that slice of the full output, bit for bit."""
+    import torch
+    import quantized_gemm_amd as q
+    p = w4a4_problem("tiny")
+    layer = Layer(p, gpu)
+    qact, ascale, t, y = layer.run(p["x_bits"], gpu)
+    K = p["x"].shape[1]
+    for n0, n1 in [(0, 16), (128, 384), (496, 512)]:
+        qw = layer.qw.view(-1, K // 2)[n0:n1].contiguous()
+        sw = layer.sw[:, n0:n1].contiguous()
+        l2t = layer.l2t[n0:n1].contiguous()
+        b = layer.bias[n0:n1].contiguous()
+        ys = q.svdq_linear_w4a4(qact, ascale, qw, sw, t, l2t, b)
+        torch.cuda.synchronize()
+        assert torch.equal(ys.view(torch.int16), y[:, n0:n1].contiguous().view(torch.int16))
+
+
+def test_activation_edge_values(gpu):
+    """Zero rows, subnormal scales (including one where the clamp to -8 / 7 is live), exact
+    half-integer quotients with an inexact reciprocal, and huge outliers: codes and scales
+    bit-exact."""
+    import torch
+    import quantized_gemm_amd as q
+    rng = np.random.default_rng(31)
+    M, K = 48, 256
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[3] = 0.0                                                   # zero token
+    x[5, :64] = 0.0
+    x[5, 0] = np.float32(9 * 2.0 ** -130)                        # scale subnormal after /7
+    x[6, 64:128] = np.float32(2.0 ** -133) * rng.integers(-9, 10, 64).astype(np.float32)
+    x[7, :64] = np.float32(2.0 ** -133) * rng.integers(-9, 10, 64).astype(np.float32)
+    x[7, 0], x[7, 1] = np.float32(-9 * 2.0 ** -133), np.float32(9 * 2.0 ** -133)
+    # scale 9/32 (absmax 63/32 = 14 * 9/64): values c * 9/64 give quotients c / 2
+    half = np.array([14, 5, -5, 7, -7, 3, 1, -1, 9, 11, 13, -13], np.float32) * np.float32(9.0 / 64.0)
+    x[8, :12] = half
+    x[8, 12:64] = np.float32(2 * 9.0 / 64.0)
+    x[9, :] *= 1e4
+    xb = synth.bf16_bits_from_f32(x)
+    xv = synth.f32_from_bf16_bits(xb)
+    tiny_first_group = np.ones(K, np.float32)
+    tiny_first_group[:64] = np.float32(2.0 ** -16)               # x_hat = c * 2^-149: scale 2^-149
+    invs = [np.ones(K, np.float32), (1.0 / rng.uniform(0.5, 3, K)).astype(np.float32), tiny_first_group]
+    for n, inv in enumerate(invs):
+        qa, sa, _ = oracle.quantize_activations(xv, inv, None)
+        qact, ascale, _ = q.svdq_quantize_act(to_dev_bf16(xb, gpu), to_dev(inv, gpu), None)
+        torch.cuda.synchronize()
+        assert np.array_equal(decode_qact(qact.cpu().numpy(), M, K), qa), f"codes differ (inv #{n})"
+        assert np.array_equal(ascale.cpu().numpy().view(np.uint32), sa.view(np.uint32)), f"scales differ (inv #{n})"
+        if n == 0:
+            assert qa[8, :12].tolist() == [7, 2, -2, 4, -4, 2, 0, 0, 4, 6, 6, -6]
+        if n == 2:
+            assert qa[7, 0] == -8 and qa[7, 1] == 7          # clamp live on both ends
+
+
+def test_no_smoothing_pointer(gpu):
+    import torch
+    import quantized_gemm_amd as q
+    p = w4a4_problem("tiny")
+    M, K = p["x"].shape
+    qa, sa, _ = oracle.quantize_activations(p["x"], np.ones(K, np.float32), None)
+    qact, ascale, _ = q.svdq_quantize_act(to_dev_bf16(p["x_bits"], gpu), None, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(decode_qact(qact.cpu().numpy(), M, K), qa)
+    assert np.array_equal(ascale.cpu().numpy(), sa)
+
+
+# ---------------------------------------------------------------------------------------------
+# W4A16 projection
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,with_bias", [(16, False), (16, True), (1, False), (5, True), (33, False)])
+def test_w4a16_parity(gpu, M, with_bias):
+    import torch
+    import quantized_gemm_amd as q
+    say(f"[w4a16 parity] M={M} bias={with_bias}")
+    p = w4a16_problem("awq", M=M, with_bias=with_bias)
+    qw, s = q.svdq_pack_weights(q.SVDQ_FMT_W4A16_BF16SCALE, p["w"])
+    assert np.array_equal(synth.f32_from_bf16_bits(s), p["scales"])
+    x = to_dev_bf16(p["x_bits"], gpu)
+    b = None if p["bias"] is None else to_dev_bf16(synth.bf16_bits_from_f32(p["bias"]), gpu)
+    y = q.awq_linear_w4a16(x, to_dev(qw, gpu), to_dev_bf16(s, gpu), b)
+    y2 = q.awq_linear_w4a16(x, to_dev(qw, gpu), to_dev_bf16(s, gpu), b)
+    torch.cuda.synchronize()
+    mx, mean = tolerance_report(bf16_to_np(y), p["y"])
+    say(f"  Y max|err|/max|Y| = {mx:.3e}, mean rel = {mean:.3e}")
+    assert mx <= MAX_REL and mean <= MEAN_REL
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))

@@ -1,0 +1,187 @@
+"""CPU tests of the C ABI library: symbol exports, argument validation, and the host packer
+checked bit for bit against the oracle (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HEADER = os.path.join(os.path.dirname(HERE), "include", "svdq.h")
+
+q = pytest.importorskip("quantized_gemm_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return q.load_library()
+    except RuntimeError as e:
+        pytest.fail(str(e))
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\**([a-z_0-9]+)\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert {"svdq_quantize_act", "svdq_linear_w4a4", "awq_linear_w4a16", "svdq_pack_weights",
+            "svdq_pack_lowrank", "svdq_debug_group_sums"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.svdq_abi_version() == 1
+
+
+# ---------------------------------------------------------------------------------------------
+# decoders written from the layout description in include/svdq.h
+# ---------------------------------------------------------------------------------------------
+def decode_w4a4(packed: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """[rows, K/2] bytes, low nibble = even k, two's complement -> int8 [rows, K]."""
+    b = packed.reshape(rows, K // 2).astype(np.int16)
+    lo = b & 0xF
+    hi = (b >> 4) & 0xF
+    out = np.empty((rows, K), np.int16)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    out[out >= 8] -= 16
+    return out.astype(np.int8)
+
+
+def decode_w4a16(packed: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Block layout -> int8 codes [K, N]."""
+    G = K // 64
+    words = packed.view(np.uint32)
+    shifts = [0, 16, 4, 20, 8, 24, 12, 28]
+    codes = np.empty((K, N), np.int8)
+    for n in range(N):
+        t, i = divmod(n, 16)
+        for k in range(K):
+            g, kk = divmod(k, 64)
+            h, rem = divmod(kk, 32)
+            j, s = divmod(rem, 8)
+            lane = i + 16 * j
+            w = int(words[((t * G + g) * 64 + lane) * 2 + h])
+            codes[k, n] = ((w >> shifts[s]) & 0xF) - 8
+    return codes
+
+
+def test_pack_w4a4_bit_exact_vs_oracle(lib):
+    rng = np.random.default_rng(21)
+    K, N = 256, 48
+    r = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    r[64:128, 5] = 0.0                                     # zero group
+    r[128:192, 7] = np.float32(3e-44) * rng.standard_normal(64).astype(np.float32)  # subnormal scale
+    r[:, 9] *= 1e3
+    qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, r)
+    oc, os_ = oracle.quantize_weights_w4a4(r)
+    assert np.array_equal(sw, os_)
+    codes = decode_w4a4(qw, N, K).T
+    assert np.array_equal(codes, oc)
+    assert codes.min() >= -8 and codes.max() <= 7
+
+
+def test_pack_w4a4_on_layer_residual(lib):
+    cfg = synth.CONFIGS["tiny"]
+    inp = synth.make_layer_inputs(cfg)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    d = oracle.svdq_decompose(x, w, cfg.rank)
+    qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, d["resid"])
+    oc, os_ = oracle.quantize_weights_w4a4(d["resid"])
+    assert np.array_equal(sw, os_)
+    assert np.array_equal(decode_w4a4(qw, cfg.N, cfg.K).T, oc)
+
+
+def test_pack_w4a16_bit_exact_vs_oracle(lib):
+    rng = np.random.default_rng(22)
+    K, N = 128, 32
+    w = oracle.bf16_round((rng.standard_normal((K, N)) * 0.02).astype(np.float32))
+    w[:64, 3] = 0.0
+    qw, s = q.svdq_pack_weights(q.SVDQ_FMT_W4A16_BF16SCALE, w)
+    oc, os_ = oracle.quantize_weights_w4a16(w)
+    assert np.array_equal(synth.f32_from_bf16_bits(s), os_)
+    assert np.array_equal(decode_w4a16(qw, K, N), oc)
+
+
+def test_pack_lowrank_bit_exact(lib):
+    rng = np.random.default_rng(23)
+    K, N, r = 128, 64, 32
+    l1 = rng.standard_normal((K, r)).astype(np.float32)
+    l2 = rng.standard_normal((r, N)).astype(np.float32)
+    l1t, l2t = q.svdq_pack_lowrank(l1, l2)
+    assert np.array_equal(synth.f32_from_bf16_bits(l1t), oracle.bf16_round(l1).T)
+    assert np.array_equal(synth.f32_from_bf16_bits(l2t), oracle.bf16_round(l2).T)
+
+
+def test_product_prep_matches_oracle_prep():
+    from quantized_gemm_amd import prep
+    cfg = synth.CONFIGS["tiny"]
+    inp = synth.make_layer_inputs(cfg)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    d = oracle.svdq_decompose(x, w, cfg.rank)
+    p = prep.decompose(x, w, cfg.rank)
+    assert np.array_equal(p["inv_smooth"], d["inv"])
+    # the same LAPACK routine on the same matrix: identical factors
+    assert np.array_equal(p["l1"], d["l1_bf16"]) and np.array_equal(p["l2"], d["l2_bf16"])
+    assert np.array_equal(p["resid"], d["resid"])
+
+
+# ---------------------------------------------------------------------------------------------
+# argument validation (checked before any HIP call, so it runs without a GPU)
+# ---------------------------------------------------------------------------------------------
+P = 0x10000  # a 16-byte-aligned dummy address; never dereferenced on the error paths below
+ODD = 0x10008
+
+
+def test_packer_validation(lib):
+    assert lib.svdq_pack_weights(7, P, 64, 16, P, P) == -4
+    assert lib.svdq_pack_weights(0, None, 64, 16, P, P) == -1
+    assert lib.svdq_pack_weights(0, P, 65, 16, P, P) == -2
+    assert lib.svdq_pack_weights(1, P, 64, 8, P, P) == -2
+    assert lib.svdq_pack_lowrank(P, P, 64, 16, 8, P, P) == -3
+    assert lib.svdq_pack_lowrank(P, P, 64, 16, 272, P, P) == -3
+    assert lib.svdq_packed_weight_bytes(0, 64, 16) == 512
+    assert lib.svdq_scale_bytes(0, 128, 16) == 128 and lib.svdq_scale_bytes(1, 128, 16) == 64
+    assert lib.svdq_scale_bytes(3, 128, 16) == 0 and lib.svdq_packed_weight_bytes(0, 100, 16) == 0
+
+
+def test_device_entry_validation(lib):
+    # svdq_quantize_act(x, M, K, inv, l1t, r, qact, ascale, lora, stream)
+    assert lib.svdq_quantize_act(None, 16, 64, None, None, 0, P, P, None, None) == -1
+    assert lib.svdq_quantize_act(ODD, 16, 64, None, None, 0, P, P, None, None) == -1
+    assert lib.svdq_quantize_act(P, 0, 64, None, None, 0, P, P, None, None) == -2
+    assert lib.svdq_quantize_act(P, 16, 96, None, None, 0, P, P, None, None) == -2
+    assert lib.svdq_quantize_act(P, 16, 64, None, P, 24, P, P, P, None) == -3
+    assert lib.svdq_quantize_act(P, 16, 64, None, P, 0, P, P, None, None) == -3
+    assert lib.svdq_quantize_act(P, 16, 64, None, P, 32, P, P, None, None) == -3
+    # svdq_linear_w4a4(qa, sa, qw, sw, lora, l2t, r, bias, y, M, N, K, stream)
+    assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, None, None, 16, 16, 64, None) == -1
+    assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, None, P, 16, 24, 64, None) == -2
+    assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, None, P, 16, 16, 0, None) == -2
+    assert lib.svdq_linear_w4a4(P, P, P, P, P, None, 32, None, P, 16, 16, 64, None) == -3
+    assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, ODD, P, 16, 16, 64, None) == -1
+    # awq_linear_w4a16(x, qw, scales, bias, y, M, N, K, stream)
+    assert lib.awq_linear_w4a16(P, None, P, None, P, 16, 16, 64, None) == -1
+    assert lib.awq_linear_w4a16(P, P, P, None, P, 16, 17, 64, None) == -2
+    # svdq_debug_group_sums(qa, qw, M, N, K, m0, n0, tm, tn, out, stream)
+    assert lib.svdq_debug_group_sums(P, P, 16, 16, 64, 8, 0, 16, 16, P, None) == -2
+    assert lib.svdq_debug_group_sums(P, P, 16, 16, 64, 0, 0, 0, 16, P, None) == -2
+
+
+def test_valid_arguments_without_gpu_report_arch(lib):
+    """With valid arguments the next check is the device; this container has no GPU."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.svdq_check_device() == -5
+    assert lib.svdq_quantize_act(P, 16, 64, None, None, 0, P, P, None, None) == -5
+    assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, None, P, 16, 16, 64, None) == -5
+    assert lib.awq_linear_w4a16(P, P, P, None, P, 16, 16, 64, None) == -5
