@@ -138,7 +138,7 @@ def main():
     l1t_d = bf16_dev(l1t) if r else None
     l2t_d = bf16_dev(l2t) if r else None
     bias_d = bf16_dev(inp["bias"])
-    qact = [torch.empty((M, K // 2), dtype=torch.uint8, device=dev) for _ in range(R)]
+    qact = [torch.empty((K // 64, M, 32), dtype=torch.uint8, device=dev) for _ in range(R)]
     asc = [torch.empty((K // 64, M), dtype=torch.float32, device=dev) for _ in range(R)]
     tl = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) if r else None for _ in range(R)]
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)

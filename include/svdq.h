@@ -45,10 +45,12 @@
  *               (one float32 multiply, round to nearest even). NULL means all ones.
  *   L1t         bf16 [r, K]: L1 transposed.   L2t  bf16 [N, r]: L2 transposed.
  *   T           bf16 [M, r]: T = bf16( bf16(X_hat) L1 ), float32 accumulation.
- *   Packed W4A4 codes (activations "qact" [M, K/2] and residual weights "qweight" [N, K/2]):
- *               byte (row, k/2) holds the code of element k (even) in bits 0-3 and of element
- *               k+1 in bits 4-7, each as a 4-bit two's-complement integer in [-8, 7]. A weight
- *               row is one output column n (K contiguous), as in nn.Linear.
+ *   Packed W4A4 codes (activations "qact", M rows; residual weights "qweight", N rows; a
+ *               weight row is one output column n): K*rows/2 bytes, group-major: the 32 bytes of
+ *               (group g, row) start at byte (g*rows + row)*32, and byte b of them holds the code
+ *               of k = 64g + 2b in bits 0-3 and of k = 64g + 2b + 1 in bits 4-7, each a 4-bit
+ *               two's-complement integer in [-8, 7]. (One group of a tile of rows is contiguous,
+ *               like the scales below.)
  *   ascale      float32 [K/64, M]: activation scale of (group g, token m) at g*M + m.
  *   wscale      float32 [K/64, N]: residual-weight scale of (group g, column n) at g*N + n.
  *   bias        bf16 [N] or NULL.           Y  bf16 [M, N].
@@ -113,7 +115,7 @@ size_t svdq_scale_bytes(int fmt, int64_t K, int64_t N);
 /* Quantize a float32 weight w [K, N] (row-major, x @ w convention) to INT4 with the rule above,
  * group 64 along K per column n, and write the packed codes and scales in the format's layout.
  *   SVDQ_FMT_W4A4_F32SCALE: w is the residual R = W_hat - L1 L2 (overview figure, stage 3);
- *     qweight_out [N, K/2] bytes, scales_out float32 [K/64, N].
+ *     qweight_out: K*N/2 bytes, group-major W4A4 code layout; scales_out float32 [K/64, N].
  *   SVDQ_FMT_W4A16_BF16SCALE: w is the plain weight of an awq_w4a16 projection;
  *     qweight_out in the W4A16 block layout, scales_out bf16 [K/64, N].
  * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE (K % 64, N % 16), SVDQ_ERR_FORMAT. */
@@ -130,7 +132,7 @@ int svdq_pack_lowrank(const float* l1, const float* l2, int64_t K, int64_t N, in
  * ------------------------------------------------------------------------------------------- */
 
 /* Fused activation step (engine figure (b): down projection + quantize on one read of X).
- * Reads X once, forms X_hat = X * inv_smooth, and writes the INT4 codes (qact [M, K/2]), the
+ * Reads X once, forms X_hat = X * inv_smooth, and writes the INT4 codes (qact, K*M/2 bytes, group-major), the
  * per-token group scales (ascale [K/64, M]) and, when r > 0, the 16-bit low-rank activation
  * T = bf16(bf16(X_hat) L1) (lora_act [M, r]) from l1t [r, K].
  * r == 0 requires l1t == NULL and lora_act == NULL; r > 0 requires both.

@@ -167,7 +167,7 @@ def svdq_quantize_act(x, inv_smooth, l1t, qact=None, ascale=None, lora_act=None,
     r = 0 if l1t is None else l1t.shape[0]
     dev = x.device
     if qact is None:
-        qact = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        qact = torch.empty((K // GROUP, M, 32), dtype=torch.uint8, device=dev)  # group-major codes
     if ascale is None:
         ascale = torch.empty((K // GROUP, M), dtype=torch.float32, device=dev)
     if r and lora_act is None:
@@ -175,18 +175,22 @@ def svdq_quantize_act(x, inv_smooth, l1t, qact=None, ascale=None, lora_act=None,
     st = load_library().svdq_quantize_act(
         _dev_ptr(x, "x", _bf16()), M, K, _dev_ptr(inv_smooth, "inv_smooth", (torch.float32,), (K,)),
         _dev_ptr(l1t, "l1t", _bf16(), (r, K) if r else None), r,
-        _dev_ptr(qact, "qact", (torch.uint8,), (M, K // 2)), _dev_ptr(ascale, "ascale", (torch.float32,), (K // GROUP, M)),
+        _dev_ptr(qact, "qact", (torch.uint8,), (K // GROUP, M, 32)),
+        _dev_ptr(ascale, "ascale", (torch.float32,), (K // GROUP, M)),
         _dev_ptr(lora_act, "lora_act", _bf16(), (M, r)) if r else None, _stream(stream))
     _check("svdq_quantize_act", st)
     return qact, ascale, (lora_act if r else None)
 
 
 def svdq_linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, bias, y=None, stream=None):
-    """Kernel (b). Returns y bf16 [M, N]."""
+    """Kernel (b). qact uint8 [K/64, M, 32] (group-major codes), ascale float32 [K/64, M],
+    qweight uint8 (K*N/2 bytes, group-major), wscale float32 [K/64, N]. Returns y bf16 [M, N]."""
     import torch
-    M, KB = qact.shape
-    K = 2 * KB
+    G, M = ascale.shape
+    K = G * GROUP
     N = wscale.shape[1]
+    if qact.numel() != M * K // 2:
+        raise ValueError("qact size does not match K*M/2")
     r = 0 if l2t is None else l2t.shape[1]
     if qweight.numel() != N * K // 2:
         raise ValueError("qweight size does not match [N, K/2]")
@@ -220,10 +224,11 @@ def awq_linear_w4a16(x, qweight, scales, bias, y=None, stream=None):
 
 
 def svdq_debug_group_sums(qact, qweight, N: int, m0: int, n0: int, tm: int, tn: int, out=None, stream=None):
-    """Exact per-group integer sums P[g, m0+i, n0+j] of the W4A4 product: int32 [K/64, tm, tn]."""
+    """Exact per-group integer sums P[g, m0+i, n0+j] of the W4A4 product: int32 [K/64, tm, tn].
+    qact uint8 [K/64, M, 32]."""
     import torch
-    M, KB = qact.shape
-    K = 2 * KB
+    G, M, _ = qact.shape
+    K = G * GROUP
     if out is None:
         out = torch.empty((K // GROUP, tm, tn), dtype=torch.int32, device=qact.device)
     st = load_library().svdq_debug_group_sums(

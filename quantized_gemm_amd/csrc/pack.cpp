@@ -80,15 +80,17 @@ void pack_w4a4(const float* w, int64_t K, int64_t N, uint8_t* q, float* scales) 
     scales[i] = s;
   }
   std::memset(q, 0, static_cast<size_t>(K * N / 2));
-  const int64_t KB = K / 2;
+  // group-major: the 32 bytes of (group g, column n) start at (g*N + n)*32
   for (int64_t k = 0; k < K; ++k) {
+    const int64_t g = k / SVDQ_GROUP;
     const float* row = w + k * N;
-    const float* srow = scales + (k / SVDQ_GROUP) * N;
+    const float* srow = scales + g * N;
     const int shift = (k & 1) ? 4 : 0;
+    uint8_t* qg = q + g * N * 32 + (k % SVDQ_GROUP) / 2;
     for (int64_t n = 0; n < N; ++n) {
       const float s = srow[n];
       const int c = (s == 0.0f) ? 0 : int4_code(row[n], s);
-      q[n * KB + k / 2] |= static_cast<uint8_t>((c & 0xF) << shift);
+      qg[n * 32] |= static_cast<uint8_t>((c & 0xF) << shift);
     }
   }
 }

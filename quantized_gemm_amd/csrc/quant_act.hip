@@ -7,6 +7,8 @@
 // float32 scales, and feeds bf16(X_hat) to bf16 MFMAs that accumulate T = X_hat L1 in float32.
 //
 // Work split: one block = 16 tokens x the whole K, 4 waves; wave w takes the groups g = w, w+4, ...
+// Codes are stored group-major (the 32 bytes of (group, token) at (g*M + m)*32), so a wave's
+// 16 tokens of one group are one contiguous 512-byte store.
 // Lane (i = lane % 16, j = lane / 16) owns token m0 + i and the 16 inputs 64g + 16j .. +15 of each
 // of its groups: 32 contiguous bytes, so a token's group is one 128-byte line spread over 4 lanes.
 // The same 16 values are the lane's two MFMA A-operands (k-slots 8j..8j+7 of two 16x16x32
@@ -55,7 +57,6 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const uint16_t* __res
   for (int c = 0; c < (NR > 0 ? NR : 1); ++c) tacc[c] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const uint16_t* xrow = x + (size_t)(row_ok ? m : 0) * K;
-  uint8_t* qrow = qact + (size_t)(row_ok ? m : 0) * (K / 2);
 
   for (int g = wave; g < G; g += kQaWaves) {
     const int k0 = g * kGroup + j * 16;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const uint16_t* __res
     w0 ^= 0x88888888u;  // offset binary -> two's complement nibbles
     w1 ^= 0x88888888u;
     if (row_ok) {
-      *reinterpret_cast<uint2*>(qrow + k0 / 2) = uint2{w0, w1};
+      *reinterpret_cast<uint2*>(qact + ((size_t)g * M + m) * 32 + 8 * j) = uint2{w0, w1};
       if (j == 0) ascale[(size_t)g * M + m] = sa;
     }
 

@@ -55,13 +55,16 @@ def w4a16_problem(name: str = "awq", M: int = None, with_bias: bool = False):
 
 
 def decode_qact(packed: np.ndarray, rows: int, K: int) -> np.ndarray:
-    """[rows, K/2] bytes (low nibble = even k, two's complement) -> int8 [rows, K]."""
-    b = np.asarray(packed, dtype=np.uint8).reshape(rows, K // 2).astype(np.int16)
-    out = np.empty((rows, K), np.int16)
-    out[:, 0::2] = b & 0xF
-    out[:, 1::2] = (b >> 4) & 0xF
+    """Group-major packed codes (the 32 bytes of (group g, row) at (g*rows + row)*32; byte b holds
+    k = 64g + 2b in its low nibble and 64g + 2b + 1 in its high nibble, two's complement)
+    -> int8 [rows, K]."""
+    G = K // 64
+    b = np.asarray(packed, dtype=np.uint8).reshape(G, rows, 32).astype(np.int16)
+    out = np.empty((rows, G, 64), np.int16)
+    out[:, :, 0::2] = (b & 0xF).transpose(1, 0, 2)
+    out[:, :, 1::2] = ((b >> 4) & 0xF).transpose(1, 0, 2)
     out[out >= 8] -= 16
-    return out.astype(np.int8)
+    return out.reshape(rows, K).astype(np.int8)
 
 
 def bf16_bits(a_f32: np.ndarray) -> np.ndarray:

@@ -183,7 +183,7 @@ def test_column_slice_invariance(gpu):
     qact, ascale, t, y = layer.run(p["x_bits"], gpu)
     K = p["x"].shape[1]
     for n0, n1 in [(0, 16), (128, 384), (496, 512)]:
-        qw = layer.qw.view(-1, K // 2)[n0:n1].contiguous()
+        qw = layer.qw.view(K // 64, -1, 32)[:, n0:n1].contiguous()
         sw = layer.sw[:, n0:n1].contiguous()
         l2t = layer.l2t[n0:n1].contiguous()
         b = layer.bias[n0:n1].contiguous()

@@ -43,13 +43,16 @@ def test_exports_every_declared_symbol(lib):
 # decoders written from the layout description in include/svdq.h
 # ---------------------------------------------------------------------------------------------
 def decode_w4a4(packed: np.ndarray, rows: int, K: int) -> np.ndarray:
-    """[rows, K/2] bytes, low nibble = even k, two's complement -> int8 [rows, K]."""
-    b = packed.reshape(rows, K // 2).astype(np.int16)
-    lo = b & 0xF
-    hi = (b >> 4) & 0xF
+    """Group-major: (group g, row) -> 32 bytes at (g*rows + row)*32, byte b = codes of
+    k = 64g + 2b (low nibble) and 64g + 2b + 1 (high nibble), two's complement -> int8 [rows, K]."""
+    G = K // 64
     out = np.empty((rows, K), np.int16)
-    out[:, 0::2] = lo
-    out[:, 1::2] = hi
+    flat = packed.reshape(-1)
+    for g in range(G):
+        for r in range(rows):
+            blk = flat[(g * rows + r) * 32:(g * rows + r) * 32 + 32].astype(np.int16)
+            out[r, 64 * g + 0:64 * g + 64:2] = blk & 0xF
+            out[r, 64 * g + 1:64 * g + 64:2] = (blk >> 4) & 0xF
     out[out >= 8] -= 16
     return out.astype(np.int8)
 
