@@ -46,6 +46,20 @@ __device__ __forceinline__ v4i mfma_i8_16x16x64(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// 32x32x32 int8: lane l supplies row (A) / column (B) l % 32 and 16 k-slots chosen by l / 32;
+// D: lane l holds column l % 32, register v holds row 8 * (v / 4) + 4 * (l / 32) + v % 4.
+__device__ __forceinline__ v16i mfma_i8_32x32x32(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// 32x32x16 bf16 (8 bf16 per lane per operand), same C/D layout as the int8 32x32 shape.
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(v8bf a, v8bf b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // 8 packed two's-complement nibbles (low nibble of each byte = even element) -> two int8x4 words
 // holding 16 * code: the byte's high nibble already sits in the int8 sign position; the low
 // nibble is shifted there. Both operands of a product use this same order, so the K pairing

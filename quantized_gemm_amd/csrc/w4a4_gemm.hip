@@ -4,8 +4,8 @@
 // product write the same output, so both accumulate into one float32 tile and Y is stored once.
 //
 // CDNA4 has no INT4 MFMA. Packed nibbles are widened to int8 holding 16 * code (two bit
-// operations per 8 codes) and fed to v_mfma_i32_16x16x64_i8, whose K of 64 is exactly one
-// quantization group, so every MFMA yields 256 * P[g] for a 16x16 tile, P being the exact integer
+// operations per 8 codes) and fed to v_mfma_i32_32x32x32_i8; two chained instructions cover one
+// quantization group of 64, so they yield 256 * P[g] for a 32x32 tile, P being the exact integer
 // group sum. The MFMA's C operand is the constant 0x4B400000 (the float 1.5 * 2^23): the integer
 // result is then the bit pattern of the float 1.5*2^23 + 256 P (exact, |256 P| <= 2^20), so no
 // int-to-float conversion is needed. The group-boundary rescale is two FMAs per element:
@@ -14,11 +14,11 @@
 // MFMAs accumulating straight into the same float32 tile (C operand = acc), adds the bias and
 // stores bf16.
 //
-// Tiling: block = 128 x 128 outputs, 4 waves (2 x 2), wave tile 64 x 64 = 4 x 4 MFMA tiles;
+// Tiling: block = 128 x 128 outputs, 4 waves (2 x 2), wave tile 64 x 64 = 2 x 2 MFMA tiles;
 // two blocks per CU. One K step is one group of 64. The block loads the group's packed codes
 // of its 128 tokens and 128 columns (4 KiB each, contiguous thanks to the group-major layout)
 // with one 16-byte load per thread, unpacks them once into LDS as int8 (rows padded to 80
-// bytes so that the 16-byte operand reads of 16 lanes hit distinct banks), together with the
+// bytes so that 16-byte operand reads of consecutive rows hit distinct banks), together with the
 // group's 128 + 128 scales. LDS is double-buffered and the global loads run two groups ahead:
 // group g+2 is in flight while group g is multiplied; one barrier per group.
 // Tile order: consecutive block ids land on different XCDs (round-robin dispatch), so block id b
@@ -88,154 +88,197 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
 
   // Loader role of this thread: 16 packed bytes (32 codes) of row lrow of the A and of the B tile,
   // plus one scale (threads 0..127: token m0 + tid, threads 128..255: column n0 + tid - 128).
+  // Rows past M (columns past N) read the last valid row instead: their outputs are never
+  // stored, so the loads need no mask. Per-thread byte offsets stay in VGPRs; the per-group
+  // slab bases are uniform, so each load is one scalar-base + vector-offset instruction.
   const int lrow = tid >> 1;
   const int lhalf = tid & 1;
-  const bool la_ok = m0 + lrow < M;
-  const bool lb_ok = n0 + lrow < N;
-  const uint8_t* ga = qa + (size_t)(la_ok ? m0 + lrow : 0) * 32 + 16 * lhalf;
-  const uint8_t* gb = qw + (size_t)(lb_ok ? n0 + lrow : 0) * 32 + 16 * lhalf;
+  const uint32_t a_off = (uint32_t)min(m0 + lrow, M - 1) * 32u + 16u * lhalf;
+  const uint32_t b_off = (uint32_t)min(n0 + lrow, N - 1) * 32u + 16u * lhalf;
   const bool s_is_a = tid < kBM;
-  const int sidx = s_is_a ? m0 + tid : n0 + tid - kBM;
-  const bool s_ok = s_is_a ? sidx < M : sidx < N;
-  const float* gs = s_is_a ? sa : sw;
-  const int sstride = s_is_a ? M : N;
-  const size_t a_gstride = (size_t)M * 32;
-  const size_t b_gstride = (size_t)N * 32;
+  const uint32_t s_off = s_is_a ? (uint32_t)min(m0 + tid, M - 1) : (uint32_t)min(n0 + tid - kBM, N - 1);
 
-  uint4 ra = {0u, 0u, 0u, 0u}, rb = {0u, 0u, 0u, 0u};
+  uint4 ra, rb;
   float rs = 0.0f;
   auto gload = [&](int g) {
-    ra = la_ok ? *reinterpret_cast<const uint4*>(ga + g * a_gstride) : uint4{0u, 0u, 0u, 0u};
-    rb = lb_ok ? *reinterpret_cast<const uint4*>(gb + g * b_gstride) : uint4{0u, 0u, 0u, 0u};
-    if constexpr (!DEBUG) rs = s_ok ? gs[(size_t)g * sstride + sidx] : 0.0f;
+    const uint8_t* qa_g = qa + (size_t)g * M * 32;
+    const uint8_t* qw_g = qw + (size_t)g * N * 32;
+    ra = *reinterpret_cast<const uint4*>(qa_g + a_off);
+    rb = *reinterpret_cast<const uint4*>(qw_g + b_off);
+    if constexpr (!DEBUG) {
+      const float* sa_g = sa + (size_t)g * M;
+      const float* sw_g = sw + (size_t)g * N;
+      rs = s_is_a ? sa_g[s_off] : sw_g[s_off];
+    }
   };
-  auto lstore = [&](int stage) {
-    uint8_t* st = lds + stage * kStageBytes;
-    uint8_t* pa = st + lrow * kPitch + 32 * lhalf;
-    *reinterpret_cast<uint4*>(pa) = unpack_chunk(ra.x, ra.y);
-    *reinterpret_cast<uint4*>(pa + 16) = unpack_chunk(ra.z, ra.w);
-    uint8_t* pb = st + (kBM + lrow) * kPitch + 32 * lhalf;
-    *reinterpret_cast<uint4*>(pb) = unpack_chunk(rb.x, rb.y);
-    *reinterpret_cast<uint4*>(pb + 16) = unpack_chunk(rb.z, rb.w);
+  // LDS byte offsets of this thread's unpacked stores and of the lane's operand / scale reads.
+  const uint32_t st_a = lrow * kPitch + 32 * lhalf;
+  const uint32_t st_b = (kBM + lrow) * kPitch + 32 * lhalf;
+  auto lstore = [&](uint8_t* st) {
+    *reinterpret_cast<uint4*>(st + st_a) = unpack_chunk(ra.x, ra.y);
+    *reinterpret_cast<uint4*>(st + st_a + 16) = unpack_chunk(ra.z, ra.w);
+    *reinterpret_cast<uint4*>(st + st_b) = unpack_chunk(rb.x, rb.y);
+    *reinterpret_cast<uint4*>(st + st_b + 16) = unpack_chunk(rb.z, rb.w);
     if constexpr (!DEBUG) reinterpret_cast<float*>(st + kScaleOff)[tid] = rs;
   };
 
-  v4f acc[4][4];
+  // Wave tile 64 x 64 = 2 x 2 MFMA tiles of 32 x 32. Lane l = 32 h + r: row / column r of a tile,
+  // k-slots 16h .. 16h+15 of each 32-wide half of the group (LDS bytes 32 s + 16 h, s = 0, 1).
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+  const uint32_t rd_a = (64 * wm + r32) * kPitch + 16 * h;
+  const uint32_t rd_b = (kBM + 64 * wn + r32) * kPitch + 16 * h;
+  const uint32_t rd_sa = kScaleOff + 4 * (64 * wm + 4 * h);
+  const uint32_t rd_sw = kScaleOff + 4 * (kBM + 64 * wn + r32);
+  v16f acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
-  const v4i magic = {(int)kMagicBits, (int)kMagicBits, (int)kMagicBits, (int)kMagicBits};
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+  v16i magic;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) magic[v] = (int)kMagicBits;
 
-  // Software pipeline: registers hold group g+1 (loaded one iteration earlier) while group g is
-  // multiplied from LDS; at the end of iteration g they go to the other LDS stage and the global
-  // loads of group g+2 are issued, so every load has a whole iteration to arrive.
-  gload(0);
-  lstore(0);
-  if (G > 1) gload(1);
-  __syncthreads();
-
-  for (int g = 0; g < G; ++g) {
-    const uint8_t* st = lds + (g & 1) * kStageBytes;
-    v4i A[4], B[4];
+  // One K step: multiply group g from LDS stage `st`, then move the registers holding group
+  // g+1 into the other stage `nx` and issue the global loads of group g+2.
+  auto step = [&](int g, const uint8_t* st, uint8_t* nx) {
+    v4i A[2][2], B[2][2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      A[a] = *reinterpret_cast<const v4i*>(st + (64 * wm + 16 * a + i) * kPitch + 16 * j);
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-      B[b] = *reinterpret_cast<const v4i*>(st + (kBM + 64 * wn + 16 * b + i) * kPitch + 16 * j);
+      for (int s2 = 0; s2 < 2; ++s2) A[a][s2] = *reinterpret_cast<const v4i*>(st + rd_a + 32 * a * kPitch + 32 * s2);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) B[b][s2] = *reinterpret_cast<const v4i*>(st + rd_b + 32 * b * kPitch + 32 * s2);
 
     if constexpr (DEBUG) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const v4i d = mfma_i8_16x16x64(A[a], B[b], magic);
-          const int n = n0 + 64 * wn + 16 * b + i;
+        for (int b = 0; b < 2; ++b) {
+          const v16i d = mfma_i8_32x32x32(A[a][1], B[b][1], mfma_i8_32x32x32(A[a][0], B[b][0], magic));
+          const int n = n0 + 64 * wn + 32 * b + r32;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int m = m0 + 64 * wm + 16 * a + 4 * j + v;
+          for (int v = 0; v < 16; ++v) {
+            const int m = m0 + 64 * wm + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
             if (m >= dm0 && m < dm0 + dtm && n >= dn0 && n < dn0 + dtn)
               dbg[((size_t)g * dtm + (m - dm0)) * dtn + (n - dn0)] = (d[v] - (int)kMagicBits) >> 8;
           }
         }
     } else {
-      const float* ss = reinterpret_cast<const float*>(st + kScaleOff);
-      float4 sav[4];
+      float sav[2][16];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) sav[a] = *reinterpret_cast<const float4*>(ss + 64 * wm + 16 * a + 4 * j);
-      float swv[4], swc[4];
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        swv[b] = ss[kBM + 64 * wn + 16 * b + i];
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = *reinterpret_cast<const float4*>(st + rd_sa + 4 * (32 * a + 8 * q));
+          sav[a][4 * q + 0] = f.x;
+          sav[a][4 * q + 1] = f.y;
+          sav[a][4 * q + 2] = f.z;
+          sav[a][4 * q + 3] = f.w;
+        }
+      float swv[2], swc[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        swv[b] = *reinterpret_cast<const float*>(st + rd_sw + 4 * 32 * b);
         swc[b] = -kMagic * swv[b];
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float s4[4] = {sav[a].x, sav[a].y, sav[a].z, sav[a].w};
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const v4i d = mfma_i8_16x16x64(A[a], B[b], magic);
+        for (int b = 0; b < 2; ++b) {
+          const v16i d = mfma_i8_32x32x32(A[a][1], B[b][1], mfma_i8_32x32x32(A[a][0], B[b][0], magic));
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
+          for (int v = 0; v < 16; ++v) {
             const float u = __builtin_fmaf(__int_as_float(d[v]), swv[b], swc[b]);
-            acc[a][b][v] = __builtin_fmaf(u, s4[v], acc[a][b][v]);
+            acc[a][b][v] = __builtin_fmaf(u, sav[a][v], acc[a][b][v]);
           }
         }
-      }
     }
-    if (g + 1 < G) lstore((g + 1) & 1);
-    if (g + 2 < G) gload(g + 2);
+    // The next stage is always written and the loads always issued (clamped to the last group):
+    // the step stays one basic block, and a stage written after the last group is never read.
+    lstore(nx);
+    gload(min(g + 2, G - 1));
+    if constexpr (!DEBUG) {
+      // Issue order within the wave: operand and scale reads; the MFMAs of the first two tiles
+      // with the unpack and LDS stores of the next stage beside them; the next global loads; the
+      // last two tiles' MFMAs each followed by 16 rescale FMAs of the finished tiles; the rest of
+      // the rescale. The matrix core and the VALU thus work at the same time within one wave.
+      __builtin_amdgcn_sched_group_barrier(0x100, 17, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 26, 0);  // VALU: unpack
+      __builtin_amdgcn_sched_group_barrier(0x200, 5, 0);   // LDS writes
+      __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);   // global loads
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0); // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 80, 0);  // VALU
+    }
     __syncthreads();
+  };
+
+  // Software pipeline: registers hold group g+1 (loaded one step earlier) while group g is
+  // multiplied from LDS; every global load has a whole step to arrive.
+  gload(0);
+  lstore(lds);
+  gload(min(1, G - 1));
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const uint32_t cur = (g & 1) * kStageBytes;
+    step(g, lds + cur, lds + (kStageBytes - cur));
   }
 
   if constexpr (!DEBUG) {
     const int wm0 = m0 + 64 * wm;
     const int wn0 = n0 + 64 * wn;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[a][b][v] = acc[a][b][v] * (1.0f / 256.0f);
+        for (int v = 0; v < 16; ++v) acc[a][b][v] = acc[a][b][v] * (1.0f / 256.0f);
 
     if constexpr (NR > 0) {
-      // T L2 with K = r in steps of 32; lane group j supplies rank indices 32q + 8j .. +7 of both
-      // operands (zeros past r), accumulating into the same float32 tile.
+      // T L2 with K = r in steps of 16 on 32x32x16 bf16 MFMAs; lane (r32, h) supplies rank
+      // indices 16q + 8h .. +7 of row/column r32, accumulating into the same float32 tile.
 #pragma unroll
-      for (int q = 0; q < (NR + 1) / 2; ++q) {
-        const int k0 = 32 * q + 8 * j;
-        const bool kok = k0 < r;
-        uint4 ta[4], lb[4];
+      for (int q = 0; q < NR; ++q) {
+        const int k0 = 16 * q + 8 * h;
+        uint4 ta[2], lb[2];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int m = wm0 + 16 * a + i;
-          ta[a] = (kok && m < M) ? *reinterpret_cast<const uint4*>(tlr + (size_t)m * r + k0) : uint4{0u, 0u, 0u, 0u};
+        for (int a = 0; a < 2; ++a) {
+          const int m = wm0 + 32 * a + r32;
+          ta[a] = m < M ? *reinterpret_cast<const uint4*>(tlr + (size_t)m * r + k0) : uint4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int n = wn0 + 16 * b + i;
-          lb[b] = (kok && n < N) ? *reinterpret_cast<const uint4*>(l2t + (size_t)n * r + k0) : uint4{0u, 0u, 0u, 0u};
+        for (int b = 0; b < 2; ++b) {
+          const int n = wn0 + 32 * b + r32;
+          lb[b] = n < N ? *reinterpret_cast<const uint4*>(l2t + (size_t)n * r + k0) : uint4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) acc[a][b] = mfma_bf16_16x16x32(as_v8bf(ta[a]), as_v8bf(lb[b]), acc[a][b]);
+          for (int b = 0; b < 2; ++b) acc[a][b] = mfma_bf16_32x32x16(as_v8bf(ta[a]), as_v8bf(lb[b]), acc[a][b]);
       }
     }
 
-    // Bias, bf16 rounding and the store. MFMA C/D layout: lane (i, j), register v -> row 4j + v,
-    // column i of the 16 x 16 tile. The wave's 64 x 64 bf16 tile goes through LDS (the stage
-    // buffers are free after the last barrier) so that each lane writes 16 contiguous bytes.
+    // Bias, bf16 rounding and the store. The wave's 64 x 64 bf16 tile goes through LDS (the
+    // stage buffers are free after the last barrier) so that each lane writes 16 contiguous bytes.
     uint16_t* tile = reinterpret_cast<uint16_t*>(lds) + wave * (64 * 72);  // 64 rows x (64 + 8) bf16
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int n = wn0 + 16 * b + i;
+    for (int b = 0; b < 2; ++b) {
+      const int n = wn0 + 32 * b + r32;
       const float bv = (bias != nullptr && n < N) ? bf16_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) tile[(16 * a + 4 * j + v) * 72 + 16 * b + i] = f32_to_bf16(acc[a][b][v] + bv);
+        for (int v = 0; v < 16; ++v)
+          tile[(32 * a + 8 * (v >> 2) + 4 * h + (v & 3)) * 72 + 32 * b + r32] = f32_to_bf16(acc[a][b][v] + bv);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
