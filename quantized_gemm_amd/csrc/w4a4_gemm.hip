@@ -14,16 +14,22 @@
 // MFMAs accumulating straight into the same float32 tile (C operand = acc), adds the bias and
 // stores bf16.
 //
-// Tiling: block = 128 x 128 outputs, 4 waves (2 x 2), wave tile 64 x 64 = 2 x 2 MFMA tiles;
-// two blocks per CU. One K step is one group of 64. The block loads the group's packed codes
-// of its 128 tokens and 128 columns (4 KiB each, contiguous thanks to the group-major layout)
-// with one 16-byte load per thread, unpacks them once into LDS as int8 (rows padded to 80
-// bytes so that 16-byte operand reads of consecutive rows hit distinct banks), together with the
-// group's 128 + 128 scales. LDS is double-buffered and the global loads run two groups ahead:
-// group g+2 is in flight while group g is multiplied; one barrier per group.
+// Tiling: block = 128 x 128 outputs, 4 waves stacked along M; wave tile 32 tokens x 128 columns
+// = 1 x 4 MFMA tiles of 32 x 32; two blocks per CU. One K step is one group of 64.
+//   * Activations: each wave owns its 32 tokens, so it loads their packed codes straight from
+//     global memory (group-major layout: 1 KiB contiguous per wave and group, one 16-byte load per
+//     lane), two groups ahead, and widens them in registers.
+//   * Residual weights are shared by the 4 waves: the block loads the group's 128 columns (4 KiB,
+//     one 16-byte load per thread, two groups ahead), widens them once into LDS as int8 (rows
+//     padded to 80 bytes: conflict-free 16-byte operand reads) beside the group's 128 + 128 scales.
+//     Three LDS stages, one barrier per group.
+//   * Within a wave the rescale of group g-1 is interleaved with the MFMAs of group g: the FMAs
+//     never wait for a fresh MFMA result and the matrix core runs under the VALU work.
 // Tile order: consecutive block ids land on different XCDs (round-robin dispatch), so block id b
 // is mapped to a contiguous range of tiles per XCD, and tiles are walked in groups of 8 tile rows
-// so that the blocks resident on one XCD share their A and B tiles in that XCD's L2.
+// so that the blocks resident on one XCD share their activation and weight tiles in its L2.
+#include <type_traits>
+
 #include "svdq_device.h"
 #include "svdq_launch.h"
 
@@ -34,9 +40,12 @@ namespace {
 constexpr int kBM = 128;
 constexpr int kBN = 128;
 constexpr int kThreads = 256;
-constexpr int kPitch = 80;  // bytes per unpacked LDS row: 64 int8 codes + 16 bytes of padding
-constexpr int kScaleOff = (kBM + kBN) * kPitch;
+constexpr int kPitch = 80;  // bytes per widened LDS weight row: 64 int8 codes + 16 bytes of padding
+constexpr int kScaleOff = kBN * kPitch;                    // sa[128] then sw[128]
 constexpr int kStageBytes = kScaleOff + (kBM + kBN) * 4;
+constexpr int kEpiPitch = kBN + 8;                         // bf16 per row of the output staging tile
+constexpr int kStages = 3;
+constexpr int kLdsBytes = (kStages * kStageBytes > kBM * kEpiPitch * 2) ? kStages * kStageBytes : kBM * kEpiPitch * 2;
 constexpr int kNumXcd = 8;
 constexpr int kGroupRows = 8;
 
@@ -59,6 +68,9 @@ __device__ __forceinline__ uint4 unpack_chunk(uint32_t w0, uint32_t w1) {
   return uint4{(uint32_t)o0, (uint32_t)e0, (uint32_t)o1, (uint32_t)e1};
 }
 
+template <typename T>
+__device__ __forceinline__ v4i as_v4i(T u) { return __builtin_bit_cast(v4i, u); }
+
 // DEBUG replaces the rescale and the epilogue by a dump of the exact group sums of a window.
 template <int NR, bool DEBUG>
 __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
@@ -66,13 +78,11 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
     const float* __restrict__ sw, const uint16_t* __restrict__ tlr, const uint16_t* __restrict__ l2t, int r,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n,
     int32_t* __restrict__ dbg, int dm0, int dn0, int dtm, int dtn) {
-  __shared__ __align__(16) uint8_t lds[2 * kStageBytes];
+  __shared__ __align__(16) uint8_t lds[kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int i = lane & 15;
-  const int j = lane >> 4;
   int tm, tn;
   if constexpr (DEBUG) {
     tm = blockIdx.y + dm0 / kBM;
@@ -82,214 +92,223 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
   }
   const int m0 = tm * kBM;
   const int n0 = tn * kBN;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
   const int G = K / kGroup;
 
-  // Loader role of this thread: 16 packed bytes (32 codes) of row lrow of the A and of the B tile,
-  // plus one scale (threads 0..127: token m0 + tid, threads 128..255: column n0 + tid - 128).
-  // Rows past M (columns past N) read the last valid row instead: their outputs are never
-  // stored, so the loads need no mask. Per-thread byte offsets stay in VGPRs; the per-group
-  // slab bases are uniform, so each load is one scalar-base + vector-offset instruction.
+  // Lane l = 32 h + r of the 32x32x32 MFMA: row (A) / column (B) r, and for MFMA s = 0, 1 the 16
+  // codes of 16-code chunk 2h + s of the group (the same chunk for A and B: the k pairing matches).
+  const int r32 = lane & 31;
+  const int h = lane >> 5;
+  const int wrow = 32 * wave;                                  // the wave's first token in the tile
+
+  // Activation loads: lane reads packed bytes [16h, 16h+16) (chunks 2h, 2h+1) of its token's group.
+  // Tokens past M read the last valid token: their outputs are never stored.
+  const uint32_t a_off = (uint32_t)min(m0 + wrow + r32, M - 1) * 32u + 16u * h;
+  // Loader role (block-wide): 16 packed bytes of weight row lrow, and one scale.
   const int lrow = tid >> 1;
   const int lhalf = tid & 1;
-  const uint32_t a_off = (uint32_t)min(m0 + lrow, M - 1) * 32u + 16u * lhalf;
   const uint32_t b_off = (uint32_t)min(n0 + lrow, N - 1) * 32u + 16u * lhalf;
   const bool s_is_a = tid < kBM;
   const uint32_t s_off = s_is_a ? (uint32_t)min(m0 + tid, M - 1) : (uint32_t)min(n0 + tid - kBM, N - 1);
+  const uint32_t st_b = lrow * kPitch + 32 * lhalf;
+  // Operand / scale read offsets within a stage.
+  const uint32_t rd_b = r32 * kPitch + 32 * h;
+  const uint32_t rd_sa = kScaleOff + 4 * (wrow + 4 * h);
+  const uint32_t rd_sw = kScaleOff + 4 * (kBM + r32);
 
-  uint4 ra, rb;
-  float rs = 0.0f;
-  auto gload = [&](int g) {
-    const uint8_t* qa_g = qa + (size_t)g * M * 32;
-    const uint8_t* qw_g = qw + (size_t)g * N * 32;
-    ra = *reinterpret_cast<const uint4*>(qa_g + a_off);
-    rb = *reinterpret_cast<const uint4*>(qw_g + b_off);
+
+  uint4 apk[2], bpk[2];
+  float spk[2];
+  auto gload_a = [&](int slot, int g) { apk[slot] = *reinterpret_cast<const uint4*>(qa + (size_t)g * M * 32 + a_off); };
+  auto gload_b = [&](int slot, int g) {
+    bpk[slot] = *reinterpret_cast<const uint4*>(qw + (size_t)g * N * 32 + b_off);
+    if constexpr (!DEBUG) spk[slot] = s_is_a ? sa[(size_t)g * M + s_off] : sw[(size_t)g * N + s_off];
+  };
+  auto lstore = [&](int slot, uint8_t* st) {
+    *reinterpret_cast<uint4*>(st + st_b) = unpack_chunk(bpk[slot].x, bpk[slot].y);
+    *reinterpret_cast<uint4*>(st + st_b + 16) = unpack_chunk(bpk[slot].z, bpk[slot].w);
     if constexpr (!DEBUG) {
-      const float* sa_g = sa + (size_t)g * M;
-      const float* sw_g = sw + (size_t)g * N;
-      rs = s_is_a ? sa_g[s_off] : sw_g[s_off];
+      reinterpret_cast<float*>(st + kScaleOff)[tid] = spk[slot];
     }
   };
-  // LDS byte offsets of this thread's unpacked stores and of the lane's operand / scale reads.
-  const uint32_t st_a = lrow * kPitch + 32 * lhalf;
-  const uint32_t st_b = (kBM + lrow) * kPitch + 32 * lhalf;
-  auto lstore = [&](uint8_t* st) {
-    *reinterpret_cast<uint4*>(st + st_a) = unpack_chunk(ra.x, ra.y);
-    *reinterpret_cast<uint4*>(st + st_a + 16) = unpack_chunk(ra.z, ra.w);
-    *reinterpret_cast<uint4*>(st + st_b) = unpack_chunk(rb.x, rb.y);
-    *reinterpret_cast<uint4*>(st + st_b + 16) = unpack_chunk(rb.z, rb.w);
-    if constexpr (!DEBUG) reinterpret_cast<float*>(st + kScaleOff)[tid] = rs;
-  };
 
-  // Wave tile 64 x 64 = 2 x 2 MFMA tiles of 32 x 32. Lane l = 32 h + r: row / column r of a tile,
-  // k-slots 16h .. 16h+15 of each 32-wide half of the group (LDS bytes 32 s + 16 h, s = 0, 1).
-  const int r32 = lane & 31;
-  const int h = lane >> 5;
-  const uint32_t rd_a = (64 * wm + r32) * kPitch + 16 * h;
-  const uint32_t rd_b = (kBM + 64 * wn + r32) * kPitch + 16 * h;
-  const uint32_t rd_sa = kScaleOff + 4 * (64 * wm + 4 * h);
-  const uint32_t rd_sw = kScaleOff + 4 * (kBM + 64 * wn + r32);
-  v16f acc[2][2];
+  v16f acc[4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
   v16i magic;
 #pragma unroll
   for (int v = 0; v < 16; ++v) magic[v] = (int)kMagicBits;
+  v16i D[4];     // MFMA results of the previous group, one per column tile
+  float sap[16];  // its activation scales: rows 8q + 4h + s (q, s = 0..3) of the wave's 32 tokens
+  float swp[4];   // its weight scales, one per column tile
 
-  // One K step: multiply group g from LDS stage `st`, then move the registers holding group
-  // g+1 into the other stage `nx` and issue the global loads of group g+2.
-  auto step = [&](int g, const uint8_t* st, uint8_t* nx) {
-    v4i A[2][2], B[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) A[a][s2] = *reinterpret_cast<const v4i*>(st + rd_a + 32 * a * kPitch + 32 * s2);
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) B[b][s2] = *reinterpret_cast<const v4i*>(st + rd_b + 32 * b * kPitch + 32 * s2);
-
+  // Rescale of group gp's tile t into the accumulator; for DEBUG the exact group sums are dumped.
+  auto finish_tile = [&](int gp, int t) {
     if constexpr (DEBUG) {
+      const int n = n0 + 32 * t + r32;
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const v16i d = mfma_i8_32x32x32(A[a][1], B[b][1], mfma_i8_32x32x32(A[a][0], B[b][0], magic));
-          const int n = n0 + 64 * wn + 32 * b + r32;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int m = m0 + 64 * wm + 32 * a + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (m >= dm0 && m < dm0 + dtm && n >= dn0 && n < dn0 + dtn)
-              dbg[((size_t)g * dtm + (m - dm0)) * dtn + (n - dn0)] = (d[v] - (int)kMagicBits) >> 8;
-          }
-        }
-    } else {
-      float sav[2][16];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 f = *reinterpret_cast<const float4*>(st + rd_sa + 4 * (32 * a + 8 * q));
-          sav[a][4 * q + 0] = f.x;
-          sav[a][4 * q + 1] = f.y;
-          sav[a][4 * q + 2] = f.z;
-          sav[a][4 * q + 3] = f.w;
-        }
-      float swv[2], swc[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        swv[b] = *reinterpret_cast<const float*>(st + rd_sw + 4 * 32 * b);
-        swc[b] = -kMagic * swv[b];
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wrow + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (m >= dm0 && m < dm0 + dtm && n >= dn0 && n < dn0 + dtn)
+          dbg[((size_t)gp * dtm + (m - dm0)) * dtn + (n - dn0)] = (D[t][v] - (int)kMagicBits) >> 8;
       }
+    } else {
+      const float swc = -kMagic * swp[t];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const v16i d = mfma_i8_32x32x32(A[a][1], B[b][1], mfma_i8_32x32x32(A[a][0], B[b][0], magic));
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float u = __builtin_fmaf(__int_as_float(d[v]), swv[b], swc[b]);
-            acc[a][b][v] = __builtin_fmaf(u, sav[a][v], acc[a][b][v]);
-          }
-        }
+      for (int v = 0; v < 16; ++v) {
+        const float u = __builtin_fmaf(__int_as_float(D[t][v]), swp[t], swc);
+        acc[t][v] = __builtin_fmaf(u, sap[v], acc[t][v]);
+      }
     }
-    // The next stage is always written and the loads always issued (clamped to the last group):
-    // the step stays one basic block, and a stage written after the last group is never read.
-    lstore(nx);
-    gload(min(g + 2, G - 1));
+  };
+  // Scales of the group held in stage `sp`, for the next step's rescale.
+  auto read_scales = [&](const uint8_t* sp) {
     if constexpr (!DEBUG) {
-      // Issue order within the wave: operand and scale reads; the MFMAs of the first two tiles
-      // with the unpack and LDS stores of the next stage beside them; the next global loads; the
-      // last two tiles' MFMAs each followed by 16 rescale FMAs of the finished tiles; the rest of
-      // the rescale. The matrix core and the VALU thus work at the same time within one wave.
-      __builtin_amdgcn_sched_group_barrier(0x100, 17, 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 26, 0);  // VALU: unpack
-      __builtin_amdgcn_sched_group_barrier(0x200, 5, 0);   // LDS writes
-      __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);   // global loads
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0); // VALU
+        const float4 f = *reinterpret_cast<const float4*>(sp + rd_sa + 4 * 8 * q);
+        sap[4 * q + 0] = f.x;
+        sap[4 * q + 1] = f.y;
+        sap[4 * q + 2] = f.z;
+        sap[4 * q + 3] = f.w;
       }
-      __builtin_amdgcn_sched_group_barrier(0x002, 80, 0);  // VALU
+#pragma unroll
+      for (int t = 0; t < 4; ++t) swp[t] = *reinterpret_cast<const float*>(sp + rd_sw + 4 * 32 * t);
+    }
+  };
+
+  // One K step g (C = g % 3 is the stage of group g, S = (g+1) % 3 the stage being filled,
+  // P = g & 1 the register slot): widen the wave's activation codes of group g; for each column
+  // tile, read group g's weight operands from stage C, finish the previous group's tile and issue
+  // the tile's MFMAs; store group g+1 into stage S and issue the global loads two groups ahead;
+  // finally read group g's scales (stage C) for the next step, so that their latency hides behind
+  // the barrier. Three stages make one barrier per step sufficient: the stage written in step g
+  // was last read in step g-1.
+  auto step = [&](auto cst, auto sst, auto par, int g, auto first_tag) {
+    constexpr int C = decltype(cst)::value;
+    constexpr int S = decltype(sst)::value;
+    constexpr int P = decltype(par)::value;
+    constexpr bool first = decltype(first_tag)::value;
+    const uint8_t* st = lds + C * kStageBytes;
+    const v4i A0 = as_v4i(unpack_chunk(apk[P].x, apk[P].y));
+    const v4i A1 = as_v4i(unpack_chunk(apk[P].z, apk[P].w));
+    gload_a(P, min(g + 2, G - 1));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v4i B0 = *reinterpret_cast<const v4i*>(st + rd_b + 32 * t * kPitch);
+      const v4i B1 = *reinterpret_cast<const v4i*>(st + rd_b + 32 * t * kPitch + 16);
+      if (!first) finish_tile(g - 1, t);
+      D[t] = mfma_i8_32x32x32(A1, B1, mfma_i8_32x32x32(A0, B0, magic));
+    }
+    lstore(P ^ 1, lds + S * kStageBytes);
+    gload_b(P ^ 1, min(g + 3, G - 1));
+    read_scales(st);
+    if constexpr (!DEBUG) {
+      // Issue order: B of tile 0; A widening and its load; then per tile its rescale, the next
+      // tile's B reads and the MFMAs; the next stage's widening, LDS stores and loads; the scales.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read: B tile 0
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU: widen A
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load: A
+      constexpr int kRescale = first ? 0 : 33;
+      // tile 0
+      __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);  // VALU: rescale
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // LDS read: B tile 1
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);         // MFMA
+      // tile 1
+      __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);        // VALU: widen the next B tile
+      __builtin_amdgcn_sched_group_barrier(0x200, 3, 0);         // LDS write
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);         // global load: B, scale
+      // tile 2
+      __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      // tile 3
+      __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);         // LDS read: scales
     }
     __syncthreads();
   };
 
-  // Software pipeline: registers hold group g+1 (loaded one step earlier) while group g is
-  // multiplied from LDS; every global load has a whole step to arrive.
-  gload(0);
-  lstore(lds);
-  gload(min(1, G - 1));
+  gload_a(0, 0);
+  gload_a(1, min(1, G - 1));
+  gload_b(0, 0);
+  gload_b(1, min(1, G - 1));
+  lstore(0, lds);
+  gload_b(0, min(2, G - 1));
   __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const uint32_t cur = (g & 1) * kStageBytes;
-    step(g, lds + cur, lds + (kStageBytes - cur));
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  // Group g uses stage g % 3 and register slot g % 2: the pattern repeats every 6 groups.
+  step(I0(), I1(), I0(), 0, std::true_type());
+  int g = 1;
+  for (; g + 5 < G; g += 6) {
+    step(I1(), I2(), I1(), g, std::false_type());
+    step(I2(), I0(), I0(), g + 1, std::false_type());
+    step(I0(), I1(), I1(), g + 2, std::false_type());
+    step(I1(), I2(), I0(), g + 3, std::false_type());
+    step(I2(), I0(), I1(), g + 4, std::false_type());
+    step(I0(), I1(), I0(), g + 5, std::false_type());
   }
+  if (g < G) { step(I1(), I2(), I1(), g, std::false_type()); ++g; }
+  if (g < G) { step(I2(), I0(), I0(), g, std::false_type()); ++g; }
+  if (g < G) { step(I0(), I1(), I1(), g, std::false_type()); ++g; }
+  if (g < G) { step(I1(), I2(), I0(), g, std::false_type()); ++g; }
+  if (g < G) { step(I2(), I0(), I1(), g, std::false_type()); ++g; }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) finish_tile(G - 1, t);
 
   if constexpr (!DEBUG) {
-    const int wm0 = m0 + 64 * wm;
-    const int wn0 = n0 + 64 * wn;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[a][b][v] = acc[a][b][v] * (1.0f / 256.0f);
+      for (int v = 0; v < 16; ++v) acc[t][v] = acc[t][v] * (1.0f / 256.0f);
 
     if constexpr (NR > 0) {
       // T L2 with K = r in steps of 16 on 32x32x16 bf16 MFMAs; lane (r32, h) supplies rank
-      // indices 16q + 8h .. +7 of row/column r32, accumulating into the same float32 tile.
+      // indices 16q + 8h .. +7 of token / column r32, accumulating into the same float32 tile.
+      const int mt = min(m0 + wrow + r32, M - 1);
 #pragma unroll
       for (int q = 0; q < NR; ++q) {
         const int k0 = 16 * q + 8 * h;
-        uint4 ta[2], lb[2];
+        const uint4 ta = *reinterpret_cast<const uint4*>(tlr + (size_t)mt * r + k0);
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int m = wm0 + 32 * a + r32;
-          ta[a] = m < M ? *reinterpret_cast<const uint4*>(tlr + (size_t)m * r + k0) : uint4{0u, 0u, 0u, 0u};
+        for (int t = 0; t < 4; ++t) {
+          const int n = min(n0 + 32 * t + r32, N - 1);
+          const uint4 lb = *reinterpret_cast<const uint4*>(l2t + (size_t)n * r + k0);
+          acc[t] = mfma_bf16_32x32x16(as_v8bf(ta), as_v8bf(lb), acc[t]);
         }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int n = wn0 + 32 * b + r32;
-          lb[b] = n < N ? *reinterpret_cast<const uint4*>(l2t + (size_t)n * r + k0) : uint4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 2; ++b) acc[a][b] = mfma_bf16_32x32x16(as_v8bf(ta[a]), as_v8bf(lb[b]), acc[a][b]);
       }
     }
 
-    // Bias, bf16 rounding and the store. The wave's 64 x 64 bf16 tile goes through LDS (the
-    // stage buffers are free after the last barrier) so that each lane writes 16 contiguous bytes.
-    uint16_t* tile = reinterpret_cast<uint16_t*>(lds) + wave * (64 * 72);  // 64 rows x (64 + 8) bf16
+    // Bias, bf16 rounding and the store. MFMA C/D layout: lane (r32, h), register v -> row
+    // 8 (v / 4) + 4 h + v % 4, column r32 of a 32 x 32 tile. The block's 128 x 128 bf16 tile goes
+    // through LDS (free after the last barrier) so that each lane stores 16 contiguous bytes.
+    uint16_t* tile = reinterpret_cast<uint16_t*>(lds);
+    __syncthreads();  // every wave has finished reading the stages
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int n = wn0 + 32 * b + r32;
+    for (int t = 0; t < 4; ++t) {
+      const int n = n0 + 32 * t + r32;
       const float bv = (bias != nullptr && n < N) ? bf16_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          tile[(32 * a + 8 * (v >> 2) + 4 * h + (v & 3)) * 72 + 32 * b + r32] = f32_to_bf16(acc[a][b][v] + bv);
+      for (int v = 0; v < 16; ++v)
+        tile[(wrow + 8 * (v >> 2) + 4 * h + (v & 3)) * kEpiPitch + 32 * t + r32] = f32_to_bf16(acc[t][v] + bv);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    // 64 rows x 128 bytes: lane -> (row = 8 * pass + lane / 8, 16-byte column chunk lane % 8)
+    __syncthreads();
+    // 128 rows x 256 bytes: thread -> (row = 16 * pass + tid / 16, 16-byte chunk tid % 16)
 #pragma unroll
-    for (int pass = 0; pass < 8; ++pass) {
-      const int row = 8 * pass + (lane >> 3);
-      const int c8 = (lane & 7) * 8;
-      const int m = wm0 + row;
-      const int n = wn0 + c8;
-      const uint4 v = *reinterpret_cast<const uint4*>(tile + row * 72 + c8);
+    for (int pass = 0; pass < kBM / 16; ++pass) {
+      const int row = 16 * pass + (tid >> 4);
+      const int c8 = (tid & 15) * 8;
+      const int m = m0 + row;
+      const int n = n0 + c8;
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kEpiPitch + c8);
       if (m < M && n < N) *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = v;
     }
   }
