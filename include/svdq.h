@@ -43,7 +43,11 @@
  *   X           bf16 [M, K].
  *   inv_smooth  float32 [K]: the reciprocal smoothing factors 1/lambda_k; X_hat = float32(X) * inv
  *               (one float32 multiply, round to nearest even). NULL means all ones.
- *   L1t         bf16 [r, K]: L1 transposed.   L2t  bf16 [N, r]: L2 transposed.
+ *   L1t         r*K bf16, L1 [K, r] in MFMA operand blocks (written by svdq_pack_lowrank): the
+ *               1024-byte block ((c*(K/64) + g)*2 + h) holds, for rank columns n = 16c + i
+ *               (i = 0..15), group g and half h, lane L = i + 16*j (j = 0..3) at element 8*L + e
+ *               the value L1[64g + 32h + 8j + e][n], e = 0..7.
+ *   L2t         bf16 [N, r]: L2 transposed.
  *   T           bf16 [M, r]: T = bf16( bf16(X_hat) L1 ), float32 accumulation.
  *   Packed W4A4 codes (activations "qact", M rows; residual weights "qweight", N rows; a
  *               weight row is one output column n): K*rows/2 bytes, group-major: the 32 bytes of
@@ -122,7 +126,8 @@ size_t svdq_scale_bytes(int fmt, int64_t K, int64_t N);
 int svdq_pack_weights(int fmt, const float* w, int64_t K, int64_t N, uint8_t* qweight_out, void* scales_out);
 
 /* Round the low-rank factors to bf16 and transpose them into the kernels' operand order:
- * l1 float32 [K, r] -> l1t_out bf16 [r, K]; l2 float32 [r, N] -> l2t_out bf16 [N, r]
+ * l1 float32 [K, r] -> l1t_out (r*K bf16, the L1t block order above); l2 float32 [r, N] ->
+ * l2t_out bf16 [N, r]
  * (round to nearest even). Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_RANK. */
 int svdq_pack_lowrank(const float* l1, const float* l2, int64_t K, int64_t N, int r,
                       uint16_t* l1t_out, uint16_t* l2t_out);
@@ -134,7 +139,7 @@ int svdq_pack_lowrank(const float* l1, const float* l2, int64_t K, int64_t N, in
 /* Fused activation step (engine figure (b): down projection + quantize on one read of X).
  * Reads X once, forms X_hat = X * inv_smooth, and writes the INT4 codes (qact, K*M/2 bytes, group-major), the
  * per-token group scales (ascale [K/64, M]) and, when r > 0, the 16-bit low-rank activation
- * T = bf16(bf16(X_hat) L1) (lora_act [M, r]) from l1t [r, K].
+ * T = bf16(bf16(X_hat) L1) (lora_act [M, r]) from l1t (r*K bf16 in the L1t block order).
  * r == 0 requires l1t == NULL and lora_act == NULL; r > 0 requires both.
  * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_RANK, SVDQ_ERR_ARCH, SVDQ_ERR_LAUNCH. */
 int svdq_quantize_act(const void* x, int64_t M, int64_t K, const float* inv_smooth, const void* l1t, int r,

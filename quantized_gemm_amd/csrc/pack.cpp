@@ -161,8 +161,16 @@ int svdq_pack_lowrank(const float* l1, const float* l2, int64_t K, int64_t N, in
   if (!shape_ok(K, N)) return SVDQ_ERR_SHAPE;
   if (r < 16 || r > SVDQ_MAX_RANK || r % 16 != 0) return SVDQ_ERR_RANK;
   IeeeDenormalGuard guard;
-  for (int64_t k = 0; k < K; ++k)
-    for (int j = 0; j < r; ++j) l1t_out[static_cast<int64_t>(j) * K + k] = bf16_rne(l1[k * r + j]);
+  // L1 in MFMA operand blocks: block ((c*G + g)*2 + h) of 512 bf16; lane i + 16*jl, element e
+  // holds L1[64g + 32h + 8jl + e][16c + i].
+  const int64_t G = K / SVDQ_GROUP;
+  for (int64_t k = 0; k < K; ++k) {
+    const int64_t g = k / 64, h = (k % 64) / 32, jl = (k % 32) / 8, e = k % 8;
+    for (int n = 0; n < r; ++n) {
+      const int64_t c = n / 16, i = n % 16;
+      l1t_out[(((c * G + g) * 2 + h) * 64 + i + 16 * jl) * 8 + e] = bf16_rne(l1[k * r + n]);
+    }
+  }
   for (int j = 0; j < r; ++j)
     for (int64_t n = 0; n < N; ++n) l2t_out[n * r + j] = bf16_rne(l2[static_cast<int64_t>(j) * N + n]);
   return SVDQ_OK;

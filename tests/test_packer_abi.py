@@ -119,7 +119,18 @@ def test_pack_lowrank_bit_exact(lib):
     l1 = rng.standard_normal((K, r)).astype(np.float32)
     l2 = rng.standard_normal((r, N)).astype(np.float32)
     l1t, l2t = q.svdq_pack_lowrank(l1, l2)
-    assert np.array_equal(synth.f32_from_bf16_bits(l1t), oracle.bf16_round(l1).T)
+    # decode the L1t operand blocks (layout in include/svdq.h)
+    flat = synth.f32_from_bf16_bits(l1t.reshape(-1))
+    G = K // 64
+    dec = np.empty((K, r), np.float32)
+    for c in range(r // 16):
+        for g in range(G):
+            for hh in range(2):
+                for lane in range(64):
+                    i, jl = lane % 16, lane // 16
+                    for e in range(8):
+                        dec[64 * g + 32 * hh + 8 * jl + e, 16 * c + i] = flat[(((c * G + g) * 2 + hh) * 64 + lane) * 8 + e]
+    assert np.array_equal(dec, oracle.bf16_round(l1))
     assert np.array_equal(synth.f32_from_bf16_bits(l2t), oracle.bf16_round(l2).T)
 
 
