@@ -35,12 +35,16 @@ METRIC = "W4A4+low-rank linear TOPS (M4608 K3072 N12288 r32) & % int8 MFMA peak"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--rotate", type=int, default=10, help="buffer sets cycled through (>256 MB total)")
     ap.add_argument("--config", default="up", help="W4A4 workload from synth.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4608, help="token rows in the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the oracle sample for this long")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, run one plain device-to-device copy of this size (a known-traffic "
+                         "kernel that scales the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -67,8 +71,9 @@ def load_traffic(kernel_file: str, workload: str):
     return None
 
 
-def cpu_baseline(cfg, awq_cfg, rows: int):
-    """The oracle, as it stands, on a bounded sample of the same step (first ``rows`` tokens)."""
+def cpu_baseline(cfg, awq_cfg, rows: int, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same step (first ``rows`` tokens),
+    repeated until ``seconds`` of CPU work have been timed; the mean pass is reported."""
     import oracle
     import synth
     from threadpoolctl import threadpool_info
@@ -82,18 +87,23 @@ def cpu_baseline(cfg, awq_cfg, rows: int):
     ainp = synth.make_layer_inputs(awq_cfg)
     ax = synth.f32_from_bf16_bits(ainp["x"])
     acodes, ascales = oracle.quantize_weights_w4a16(synth.f32_from_bf16_bits(ainp["w"]))
-    t0 = time.perf_counter()
-    qa, sa, t = oracle.quantize_activations(x, d["inv"], d["l1_bf16"])
-    oracle.svdq_linear(qa, sa, qw, sw, t, d["l2_bf16"], b)
-    oracle.awq_linear(ax, acodes, ascales, None)
-    dt = time.perf_counter() - t0
+    passes, total = 0, 0.0
+    while passes == 0 or (total < seconds and passes < 100):
+        t0 = time.perf_counter()
+        qa, sa, t = oracle.quantize_activations(x, d["inv"], d["l1_bf16"])
+        oracle.svdq_linear(qa, sa, qw, sw, t, d["l2_bf16"], b)
+        oracle.awq_linear(ax, acodes, ascales, None)
+        total += time.perf_counter() - t0
+        passes += 1
+    dt = total / passes
     ops = 2.0 * rows * cfg.N * cfg.K + 2.0 * rows * cfg.rank * (cfg.K + cfg.N) + \
         2.0 * awq_cfg.M * awq_cfg.N * awq_cfg.K
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
+            "seconds_per_pass": round(dt, 4), "passes": passes,
             "sample": f"{rows} of {cfg.M} tokens of the {cfg.name} layer (activation quantization, float64 "
-                      f"dequantized product, low-rank, bias) + the full W4A16 projection M={awq_cfg.M}"}
+                      f"dequantized product, low-rank, bias) + the full W4A16 projection M={awq_cfg.M}, "
+                      f"{passes} passes, mean"}
 
 
 def main():
@@ -169,6 +179,15 @@ def main():
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n} bytes read, {n} bytes written")
+        del src, dst
 
     # timed region: exactly K steps, synchronised on both sides
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -219,16 +238,18 @@ def main():
         "kernels": {
             "svdq_quantize_act_us": round(t_a * 1e3, 2),
             "svdq_quantize_act_GBs": round(bytes_a / (t_a * 1e-3) / 1e9, 1),
+            "svdq_quantize_act_hbm_frac": round(bytes_a / (t_a * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "svdq_linear_w4a4_us": round(t_b * 1e3, 2),
             "svdq_linear_w4a4_TOPS": round(achieved_b, 2),
             "awq_linear_w4a16_us": round(t_c * 1e3, 2),
             "awq_linear_w4a16_GBs": round(bytes_c / (t_c * 1e-3) / 1e9, 1),
+            "awq_linear_w4a16_hbm_frac": round(bytes_c / (t_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "layer_TOPS_a_plus_b": round(gemm_ops / ((t_a + t_b) * 1e-3) / 1e12, 2),
         },
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle) on {args.cpu_rows} rows")
-        out["cpu_baseline"] = cpu_baseline(cfg, awq_cfg, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(cfg, awq_cfg, args.cpu_rows, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
