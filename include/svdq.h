@@ -58,12 +58,15 @@
  *   ascale      float32 [K/64, M]: activation scale of (group g, token m) at g*M + m.
  *   wscale      float32 [K/64, N]: residual-weight scale of (group g, column n) at g*N + n.
  *   bias        bf16 [N] or NULL.           Y  bf16 [M, N].
- *   Packed W4A16 weights (awq_linear_w4a16) "qweight": K*N/2 bytes in 512-byte blocks, one per
- *               (column tile t = n/16, group g), block index t*(K/64) + g. Inside a block, lane
- *               L = (n % 16) + 16*j (j = 0..3) owns 8 bytes at offset 8*L: two little-endian
- *               32-bit words h = 0, 1; word h holds the codes of k = 64g + 32h + 8j + s for
- *               s = 0..7 as offset-binary nibbles (u = code + 8), nibble s at bit offset
- *               {0, 16, 4, 20, 8, 24, 12, 28}[s].
+ *   Packed W4A16 weights (awq_linear_w4a16) "qweight": K*N/2 bytes. Column tile t = n/16 owns
+ *               the (K/64)*512 bytes starting at t*(K/64)*512. Inside a tile the groups go in
+ *               pairs: groups 2p and 2p+1 form the 1024-byte block at offset 2p*512, where lane
+ *               L = (n % 16) + 16*j (j = 0..3) owns the 16 bytes at 16*L: bytes 0..7 for group 2p,
+ *               bytes 8..15 for group 2p+1. When K/64 is odd the last group is a 512-byte block
+ *               at offset (K/64 - 1)*512 where lane L owns the 8 bytes at 8*L. A lane's 8 bytes of
+ *               group g are two little-endian 32-bit words h = 0, 1; word h holds the codes of
+ *               k = 64g + 32h + 8j + s for s = 0..7 as offset-binary nibbles (u = code + 8),
+ *               nibble s at bit offset {0, 16, 4, 20, 8, 24, 12, 28}[s].
  *   W4A16 scales  bf16 [K/64, N].
  */
 #ifndef SVDQ_H_

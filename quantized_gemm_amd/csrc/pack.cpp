@@ -98,6 +98,14 @@ void pack_w4a4(const float* w, int64_t K, int64_t N, uint8_t* q, float* scales) 
 // Nibble bit offset of slot s (0..7) inside a 32-bit word of the W4A16 block layout.
 constexpr int kW4A16NibbleShift[8] = {0, 16, 4, 20, 8, 24, 12, 28};
 
+// Byte offset of lane L's 8 bytes of group g in column tile t (W4A16 layout: group pairs in 1 KiB
+// blocks, 16 bytes per lane; an unpaired last group in a 512-byte block, 8 bytes per lane).
+int64_t w4a16_byte_offset(int64_t t, int64_t g, int64_t G, int64_t lane) {
+  const int64_t tile = t * G * 512;
+  if ((G % 2 == 1) && g == G - 1) return tile + g * 512 + 8 * lane;
+  return tile + (g & ~int64_t(1)) * 512 + 16 * lane + 8 * (g & 1);
+}
+
 void pack_w4a16(const float* w, int64_t K, int64_t N, uint8_t* q, uint16_t* scales) {
   std::vector<float> amax;
   group_absmax(w, K, N, amax);
@@ -119,8 +127,7 @@ void pack_w4a16(const float* w, int64_t K, int64_t N, uint8_t* q, uint16_t* scal
       const int c = (sc == 0.0f) ? 0 : int4_code(row[n], sc);
       const uint32_t u = static_cast<uint32_t>(c + 8) & 0xFu;
       const int64_t t = n / 16, lane = (n % 16) + 16 * jj;
-      const int64_t word = ((t * G + g) * 64 + lane) * 2 + h;
-      uint32_t* wp = reinterpret_cast<uint32_t*>(q) + word;
+      uint32_t* wp = reinterpret_cast<uint32_t*>(q + w4a16_byte_offset(t, g, G, lane)) + h;
       *wp |= u << kW4A16NibbleShift[s];
     }
   }

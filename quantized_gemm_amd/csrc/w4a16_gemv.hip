@@ -2,19 +2,25 @@
 // int4 weights, group 64, 16-bit activations, used for the memory-bound modulation projections).
 //
 // Y = bf16( X dequant(W) + b ) for a small token count (M = 16 is one MFMA row tile). The weight
-// stream dominates the traffic (0.5 byte per weight), so the kernel is organised around keeping
-// many weight loads in flight: every wave issues all the loads of a chunk of 6 groups before it
-// computes anything.
+// stream dominates the traffic (0.5 byte per weight); everything else is organised so that the
+// 16-byte weight loads run back to back.
 //
 // Dequantization without a multiply per weight: each offset-binary nibble u = code + 8 is OR-ed
 // into the bf16 pattern 0x4300, which is exactly 128 + u, and fed to a bf16 MFMA. Per (token,
 // group) the MFMA then holds sum_k x_k (128 + u_k) = sum_k x_k code_k + 136 * sum_k x_k; the second
 // term is removed with the group's input sum (taken by an MFMA against a ones operand, so it
-// arrives in the same C/D layout), and the group scale is applied in float32:
-//     acc += s[g, n] * (D - 136 * Sx[g, m]).
-// Work split: one block = one 16-token tile x 64 output columns (4 MFMA column tiles) x all of K,
-// 8 waves; wave w takes the 6-group chunks w, w + 8, ... of K. The 8 partial tiles are summed in
-// LDS in a fixed order (deterministic).
+// arrives in the same C/D layout and enters the product MFMAs as their C operand), and the group
+// scale is applied in float32:
+//     acc += s[g, n] * D,   D = MFMA(x, 128 + u) + (-136 * Sx[g, m]).
+//
+// Work split. X is tiny and read by every block, so it is loaded once per block, not once per
+// column tile: a block of kAwqWaves waves owns one 16-token row tile, wave w owns a slice of
+// kAwqPer consecutive groups of K (a chunk of kAwqWaves * kAwqPer groups at a time), and keeps
+// its slice of X and the 136 * Sx corrections in registers for the block's column tiles
+// t = blockIdx.x, blockIdx.x + gridDim.x, ... (up to kAwqMaxTiles per pass). The grid is about one
+// block per CU, and each wave issues the weight loads of all its tiles before computing. The partial
+// tiles of the waves are summed in LDS in a fixed order (deterministic) and wave 0 adds the bias
+// and stores bf16.
 #include "svdq_device.h"
 #include "svdq_launch.h"
 
@@ -23,12 +29,45 @@ namespace svdq {
 namespace {
 
 constexpr int kAwqWaves = 8;
-constexpr int kAwqColTiles = 4;
-constexpr int kChunk = 6;  // groups per load batch
+constexpr int kAwqPer = 6;        // groups per wave and K chunk (even: groups come in pairs)
+constexpr int kAwqMaxTiles = 5;   // column tiles accumulated per pass over K
+constexpr int kAwqBlocks = 256;   // target resident blocks (one per CU)
+
+static_assert(kAwqPer % 2 == 0, "weights are loaded in group pairs");
 
 __device__ __forceinline__ uint4 dequant_nibbles_bf16(uint32_t w) {
   return uint4{(w & 0x000F000Fu) | 0x43004300u, ((w >> 4) & 0x000F000Fu) | 0x43004300u,
                ((w >> 8) & 0x000F000Fu) | 0x43004300u, ((w >> 12) & 0x000F000Fu) | 0x43004300u};
+}
+
+struct TileLoad {
+  uint4 w[kAwqPer / 2];     // group pair p: .x .y = group 2p, .z .w = group 2p + 1
+  uint16_t s[kAwqPer];
+};
+
+// Weights and scales of column tile t for the groups gb .. gb + kAwqPer - 1 (indices past the last
+// group are clamped to valid data; those groups are never computed).
+__device__ __forceinline__ void load_tile(TileLoad& tl, const uint8_t* __restrict__ qw,
+                                          const uint16_t* __restrict__ scales, int t, int gb, int G, int N,
+                                          int lane, int i) {
+  const uint8_t* tile = qw + (size_t)t * G * 512;
+  const int last_pair = (G - 1) & ~1;
+#pragma unroll
+  for (int p = 0; p < kAwqPer / 2; ++p) {
+    const int g = min(gb + 2 * p, last_pair);
+    // One 16-byte load either way. An unpaired last group holds 8 bytes per lane in a 512-byte
+    // block: lane L's bytes 8L..8L+7 lie in the aligned 16 bytes at 16*(L/2) (inside the block).
+    const bool paired = g + 1 < G;
+    const int off = paired ? 16 * lane : 16 * (lane >> 1);
+    uint4 v = *reinterpret_cast<const uint4*>(tile + (size_t)g * 512 + off);
+    if (!paired && (lane & 1)) {
+      v.x = v.z;
+      v.y = v.w;
+    }
+    tl.w[p] = v;
+  }
+#pragma unroll
+  for (int q = 0; q < kAwqPer; ++q) tl.s[q] = scales[(size_t)min(gb + q, G - 1) * N + t * 16 + i];
 }
 
 __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* __restrict__ x,
@@ -37,95 +76,98 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
                                                                const uint16_t* __restrict__ bias,
                                                                uint16_t* __restrict__ y, int M, int N, int K) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar: the group slice, and with it the paired / unpaired load choice, is
+  // uniform across the wave (scalar branches, whole 16-byte loads)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15;
   const int j = lane >> 4;
-  const int nt0 = blockIdx.x * kAwqColTiles;
   const int m0 = blockIdx.y * 16;
-  const int m = m0 + i;
-  const bool row_ok = m < M;
   const int G = K / kGroup;
   const int NT = N / 16;
-  // column tiles past N (N % 64 != 0) repeat the last tile; their results are not stored
-  int nt[kAwqColTiles];
-#pragma unroll
-  for (int c = 0; c < kAwqColTiles; ++c) nt[c] = min(nt0 + c, NT - 1);
-
+  // this block's column tiles: blockIdx.x + s * gridDim.x for s < nts
+  const int nts = (NT - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  // rows past M read the last row; their results are not stored
+  const uint16_t* xrow = x + (size_t)min(m0 + i, M - 1) * K;
   const uint4 ones4 = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  v4f acc[kAwqColTiles];
-#pragma unroll
-  for (int c = 0; c < kAwqColTiles; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  __shared__ v4f red[kAwqWaves - 1][kAwqMaxTiles][kWave];
 
-  const uint16_t* xrow = x + (size_t)(row_ok ? m : 0) * K;
-  for (int g0 = wave * kChunk; g0 < G; g0 += kAwqWaves * kChunk) {
-    // Issue every load of the chunk first (groups past G repeat the last group and are skipped).
-    uint4 xa[kChunk][2];
-    uint2 wq[kChunk][kAwqColTiles];
-    uint16_t sc[kChunk][kAwqColTiles];
+  for (int tb = 0; tb < nts; tb += kAwqMaxTiles) {
+    const int nb = min(kAwqMaxTiles, nts - tb);
+    v4f acc[kAwqMaxTiles];
 #pragma unroll
-    for (int q = 0; q < kChunk; ++q) {
-      const int g = min(g0 + q, G - 1);
+    for (int s = 0; s < kAwqMaxTiles; ++s) acc[s] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int kc = 0; kc < G; kc += kAwqWaves * kAwqPer) {
+      const int gb = kc + wave * kAwqPer;
+      const int ng = max(0, min(kAwqPer, G - gb));  // groups of this wave in this chunk
+      // X slice of the wave (values 8j.. and 32+8j.. of each group: the MFMA A operands)
+      uint4 xa[kAwqPer][2];
 #pragma unroll
-      for (int c = 0; c < kAwqColTiles; ++c)
-        wq[q][c] = *reinterpret_cast<const uint2*>(qw + (((size_t)nt[c] * G + g) * kWave + lane) * 8);
-    }
+      for (int q = 0; q < kAwqPer; ++q) {
+        const int g = min(gb + q, G - 1);
+        xa[q][0] = *reinterpret_cast<const uint4*>(xrow + g * kGroup + 8 * j);
+        xa[q][1] = *reinterpret_cast<const uint4*>(xrow + g * kGroup + 32 + 8 * j);
+      }
+      // Every weight and scale load of the batch is issued before any compute: the HBM stream
+      // runs while the corrections and the first tiles are computed.
+      TileLoad tl[kAwqMaxTiles];
 #pragma unroll
-    for (int q = 0; q < kChunk; ++q) {
-      const int g = min(g0 + q, G - 1);
-      xa[q][0] = row_ok ? *reinterpret_cast<const uint4*>(xrow + g * kGroup + 8 * j) : uint4{0u, 0u, 0u, 0u};
-      xa[q][1] = row_ok ? *reinterpret_cast<const uint4*>(xrow + g * kGroup + 32 + 8 * j) : uint4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < kAwqMaxTiles; ++s)
+        if (s < nb) load_tile(tl[s], qw, scales, (int)blockIdx.x + (tb + s) * (int)gridDim.x, gb, G, N, lane, i);
+      v4f corr[kAwqPer];
 #pragma unroll
-      for (int c = 0; c < kAwqColTiles; ++c) sc[q][c] = scales[(size_t)g * N + nt[c] * 16 + i];
-    }
+      for (int q = 0; q < kAwqPer; ++q) {
+        v4f sx = mfma_bf16_16x16x32(as_v8bf(xa[q][0]), as_v8bf(ones4), v4f{0.f, 0.f, 0.f, 0.f});
+        sx = mfma_bf16_16x16x32(as_v8bf(xa[q][1]), as_v8bf(ones4), sx);
 #pragma unroll
-    for (int q = 0; q < kChunk; ++q) {
-      if (g0 + q >= G) break;
-      v4f sx = mfma_bf16_16x16x32(as_v8bf(xa[q][0]), as_v8bf(ones4), v4f{0.f, 0.f, 0.f, 0.f});
-      sx = mfma_bf16_16x16x32(as_v8bf(xa[q][1]), as_v8bf(ones4), sx);
-      float corr[4];
+        for (int v = 0; v < 4; ++v) corr[q][v] = -136.0f * sx[v];
+      }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) corr[v] = -136.0f * sx[v];
+      for (int s = 0; s < kAwqMaxTiles; ++s) {
+        if (s >= nb) break;
 #pragma unroll
-      for (int c = 0; c < kAwqColTiles; ++c) {
-        const uint4 b0 = dequant_nibbles_bf16(wq[q][c].x);
-        const uint4 b1 = dequant_nibbles_bf16(wq[q][c].y);
-        v4f d = mfma_bf16_16x16x32(as_v8bf(xa[q][0]), as_v8bf(b0), v4f{0.f, 0.f, 0.f, 0.f});
-        d = mfma_bf16_16x16x32(as_v8bf(xa[q][1]), as_v8bf(b1), d);
-        const float s = bf16_to_f32(sc[q][c]);
+        for (int q = 0; q < kAwqPer; ++q) {
+          if (q >= ng) break;
+          const uint4 wp = tl[s].w[q / 2];
+          const uint32_t w0 = (q % 2 == 0) ? wp.x : wp.z;
+          const uint32_t w1 = (q % 2 == 0) ? wp.y : wp.w;
+          // the correction enters as the MFMA's C operand: d = sum x code exactly up to rounding
+          v4f d = mfma_bf16_16x16x32(as_v8bf(xa[q][0]), as_v8bf(dequant_nibbles_bf16(w0)), corr[q]);
+          d = mfma_bf16_16x16x32(as_v8bf(xa[q][1]), as_v8bf(dequant_nibbles_bf16(w1)), d);
+          const float sc = bf16_to_f32(tl[s].s[q]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[c][v] = __builtin_fmaf(d[v] + corr[v], s, acc[c][v]);
+          for (int v = 0; v < 4; ++v) acc[s][v] = __builtin_fmaf(d[v], sc, acc[s][v]);
+        }
       }
     }
-  }
 
-  // Fixed-order reduction ((w0 + w1) + w2) + ... + w7: waves 1..7 park their tiles in LDS, wave 0
-  // sums them in order, adds the bias and stores bf16 (MFMA C/D layout: lane (i, j), register v
-  // -> row 4j + v, column i of a 16 x 16 tile).
-  __shared__ v4f red[kAwqWaves - 1][kAwqColTiles][kWave];
-  if (wave > 0) {
+    // Fixed-order reduction ((w0 + w1) + w2) + ... of the waves' partial tiles; wave 0 adds the
+    // bias and stores (MFMA C/D layout: lane (i, j), register v -> row 4j + v, column i).
+    if (wave > 0) {
 #pragma unroll
-    for (int c = 0; c < kAwqColTiles; ++c) red[wave - 1][c][lane] = acc[c];
-  }
-  __syncthreads();
-  if (wave == 0) {
+      for (int s = 0; s < kAwqMaxTiles; ++s) red[wave - 1][s][lane] = acc[s];
+    }
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
-    for (int c = 0; c < kAwqColTiles; ++c) {
-      v4f s = acc[c];
-      for (int w = 1; w < kAwqWaves; ++w) {
-        const v4f p = red[w - 1][c][lane];
+      for (int s = 0; s < kAwqMaxTiles; ++s) {
+        if (s >= nb) break;
+        v4f a = acc[s];
+        for (int w = 1; w < kAwqWaves; ++w) {
+          const v4f p = red[w - 1][s][lane];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s[v] = s[v] + p[v];
-      }
-      if (nt0 + c < NT) {
-        const int n = (nt0 + c) * 16 + i;
+          for (int v = 0; v < 4; ++v) a[v] = a[v] + p[v];
+        }
+        const int n = ((int)blockIdx.x + (tb + s) * (int)gridDim.x) * 16 + i;
         const float b = bias != nullptr ? bf16_to_f32(bias[n]) : 0.0f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int row = m0 + 4 * j + v;
-          if (row < M) y[(size_t)row * N + n] = f32_to_bf16(s[v] + b);
+          if (row < M) y[(size_t)row * N + n] = f32_to_bf16(a[v] + b);
         }
       }
     }
+    __syncthreads();  // red is reused by the next batch of tiles
   }
 }
 
@@ -134,7 +176,9 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
 hipError_t launch_w4a16(const uint16_t* x, const uint8_t* qweight, const uint16_t* scales, const uint16_t* bias,
                         uint16_t* y, int M, int N, int K, hipStream_t stream) {
   const int NT = N / 16;
-  const dim3 grid((NT + kAwqColTiles - 1) / kAwqColTiles, (M + 15) / 16);
+  const int row_tiles = (M + 15) / 16;
+  const int cols = max(1, min(NT, kAwqBlocks / row_tiles));
+  const dim3 grid(cols, row_tiles);
   hipLaunchKernelGGL(w4a16_kernel, grid, dim3(kAwqWaves * 64), 0, stream, x, qweight, scales, bias, y, M, N, K);
   return hipGetLastError();
 }

@@ -261,3 +261,24 @@ def test_w4a16_parity(gpu, M, with_bias):
     say(f"  Y max|err|/max|Y| = {mx:.3e}, mean rel = {mean:.3e}")
     assert mx <= MAX_REL and mean <= MEAN_REL
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,K,N", [(20, 448, 592), (16, 6400, 96), (300, 192, 256), (3, 64, 16)])
+def test_w4a16_shapes(gpu, M, K, N):
+    """Odd group counts (unpaired last group), K longer than one chunk of the waves' slices,
+    several row tiles, column-tile counts that leave blocks with fewer tiles, the smallest shape."""
+    import torch
+    import quantized_gemm_amd as q
+    say(f"[w4a16 shapes] M={M} K={K} N={N}")
+    x_bits = synth.random_bf16((M, K), seed=K + N)
+    w = oracle.bf16_round(synth.random_f32((K, N), seed=K * N + 1, scale=0.02))
+    b = oracle.bf16_round(synth.random_f32((N,), seed=N + 7, scale=0.01))
+    codes, s_ref = oracle.quantize_weights_w4a16(w)
+    _, y_ref = oracle.awq_linear(synth.f32_from_bf16_bits(x_bits), codes, s_ref, b)
+    qw, s = q.svdq_pack_weights(q.SVDQ_FMT_W4A16_BF16SCALE, w)
+    y = q.awq_linear_w4a16(to_dev_bf16(x_bits, gpu), to_dev(qw, gpu), to_dev_bf16(s, gpu),
+                           to_dev_bf16(synth.bf16_bits_from_f32(b), gpu))
+    torch.cuda.synchronize()
+    mx, mean = tolerance_report(bf16_to_np(y), y_ref)
+    say(f"  Y max|err|/max|Y| = {mx:.3e}, mean rel = {mean:.3e}")
+    assert mx <= MAX_REL and mean <= MEAN_REL

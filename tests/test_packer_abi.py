@@ -58,9 +58,10 @@ def decode_w4a4(packed: np.ndarray, rows: int, K: int) -> np.ndarray:
 
 
 def decode_w4a16(packed: np.ndarray, K: int, N: int) -> np.ndarray:
-    """Block layout -> int8 codes [K, N]."""
+    """W4A16 layout -> int8 codes [K, N]: per column tile, group pairs in 1 KiB blocks with 16
+    bytes per lane (8 per group); an unpaired last group is a 512-byte block, 8 bytes per lane."""
     G = K // 64
-    words = packed.view(np.uint32)
+    flat = packed.reshape(-1)
     shifts = [0, 16, 4, 20, 8, 24, 12, 28]
     codes = np.empty((K, N), np.int8)
     for n in range(N):
@@ -70,7 +71,11 @@ def decode_w4a16(packed: np.ndarray, K: int, N: int) -> np.ndarray:
             h, rem = divmod(kk, 32)
             j, s = divmod(rem, 8)
             lane = i + 16 * j
-            w = int(words[((t * G + g) * 64 + lane) * 2 + h])
+            if G % 2 == 1 and g == G - 1:
+                off = t * G * 512 + g * 512 + 8 * lane
+            else:
+                off = t * G * 512 + (g - g % 2) * 512 + 16 * lane + 8 * (g % 2)
+            w = int(flat[off + 4 * h:off + 4 * h + 4].view(np.uint32)[0])
             codes[k, n] = ((w >> shifts[s]) & 0xF) - 8
     return codes
 
@@ -102,9 +107,10 @@ def test_pack_w4a4_on_layer_residual(lib):
     assert np.array_equal(decode_w4a4(qw, cfg.N, cfg.K).T, oc)
 
 
-def test_pack_w4a16_bit_exact_vs_oracle(lib):
+@pytest.mark.parametrize("K", [128, 192])
+def test_pack_w4a16_bit_exact_vs_oracle(lib, K):
     rng = np.random.default_rng(22)
-    K, N = 128, 32
+    N = 32
     w = oracle.bf16_round((rng.standard_normal((K, N)) * 0.02).astype(np.float32))
     w[:64, 3] = 0.0
     qw, s = q.svdq_pack_weights(q.SVDQ_FMT_W4A16_BF16SCALE, w)
