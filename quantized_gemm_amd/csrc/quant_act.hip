@@ -7,20 +7,21 @@
 // float32 scales, and feeds bf16(X_hat) to bf16 MFMAs that accumulate T = X_hat L1 in float32.
 //
 // Work split: one block = 16 tokens x the whole K, 8 waves; wave w takes a contiguous eighth of the
-// groups and issues the X loads of up to 6 groups at once (the HBM stream) before computing. Each
-// load reads whole 128-byte lines (8 lanes per token); a wave-private LDS slice reorders the values
-// into the compute layout. L1^T comes in the packer's MFMA operand blocks: one 1 KiB load per
-// operand.
-// Codes are stored group-major (the 32 bytes of (group, token) at (g*M + m)*32), so a wave's
-// 16 tokens of one group are one contiguous 512-byte store.
-// Lane (i = lane % 16, j = lane / 16) owns token m0 + i and the values 8j..8j+7 and 32+8j..32+8j+7
-// of a group: exactly its A-operand k-slots of the two 16x16x32 bf16 MFMA steps (and the L1^T
-// blocks hold the B operands in the same k order). T partials of the 8 waves are summed in LDS
-// in a fixed order (deterministic).
+// groups and issues the X loads of up to 6 groups at once (the HBM stream) before computing.
+// Quantization works in the load layout: lane (rr = lane / 8, c = lane % 8) holds values
+// 8c..8c+7 of tokens m0 + rr and m0 + 8 + rr, so each load reads whole 128-byte lines, the group
+// absmax is a max over 8 consecutive lanes, and the lane's 8 codes are exactly bytes 4c..4c+3 of
+// the token's 32-byte code record (codes are group-major: the 32 bytes of (group, token) at
+// (g*M + m)*32, so a store instruction writes 8 tokens x 32 contiguous bytes).
+// The down projection needs the MFMA A layout instead (lane (i = lane % 16, j = lane / 16): token
+// m0 + i, values 8j..8j+7 and 32+8j..32+8j+7); bf16(X_hat) is re-read in that layout from a
+// wave-private LDS slice. L1^T comes in the packer's MFMA operand blocks (the same k order): one
+// 1 KiB load per operand. T partials of the 8 waves are summed in LDS in a fixed order.
 //
 // Quantization is bit-exact with the IEEE rule code = clamp(rint_even(x_hat / s), -8, 7),
-// s = absmax / 7 (IEEE division): see quantize16 for the bracket argument that lets two FMAs per
-// value decide the code, with an IEEE-division fallback for the rare undecided group.
+// s = absmax / 7 (IEEE quotient, computed without a division by div7): see quantize8x2 for the
+// bracket argument that lets two FMAs per value decide the code, with an IEEE-division fallback
+// for the rare undecided group.
 #include <float.h>
 
 #include "svdq_device.h"
@@ -33,45 +34,57 @@ namespace {
 constexpr int kQaWaves = 8;
 constexpr float kMagic8 = 12582920.0f;  // 1.5 * 2^23 + 8
 
-// Max over the 4 lanes {l, l^16, l^32, l^48} that hold one token's group (gfx950 lane swaps).
-__device__ __forceinline__ float group_max4(float a) {
-  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
-  const float b = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(b), __float_as_uint(b), false, false);
-  return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+// Max over the 8 consecutive lanes 8r .. 8r+7 that hold one token's group: xor-1 and xor-2 lane
+// exchanges inside each quad, then the mirror of the 8-lane half row (lane l <-> 7 - l).
+__device__ __forceinline__ float group_max8(float a) {
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, true)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, true)));
+  return fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x141, 0xF, 0xF, true)));
 }
 
-// Quantize the 16 values a lane holds for one (token, group) and return them packed as two words
-// of two's-complement nibbles (element 2b in bits 4b..4b+3, element 2b+1 in bits 4b+4..4b+7);
-// `sa` is the group scale shared by the 4 lanes of the token. Every lane of the wave calls it.
+// fl(a / 7) for a >= 0 without a division: q1 = a * RN(1/7), one FMA residual and one FMA
+// correction. Checked against the IEEE quotient for every non-negative finite float (subnormals
+// included) by an exhaustive host test.
+__device__ __forceinline__ float div7(float a) {
+  constexpr float kRcp7 = 0x1.24924ap-3f;  // RN(1/7)
+  const float q1 = a * kRcp7;
+  return __builtin_fmaf(__builtin_fmaf(-7.0f, q1, a), kRcp7, q1);
+}
+
+// Quantize two groups of 8 values (xh[0..7] with scale s0, xh[8..15] with scale s1) and return
+// each packed as one word of two's-complement nibbles (element e in bits 4e..4e+3).
 //
-// Fast path: rc = v_rcp_f32(sa) is within 1 ulp of 1/sa for a normal sa with a normal reciprocal,
-// so rc -/+ 6 ulps bracket 1/sa with more than 4 ulps to spare on each side; the exact products
-// x * rc_lo and x * rc_hi then bracket fl(x / sa) (which is within half an ulp of x / sa), and
+// Fast path: rc = v_rcp_f32(s) is within 1 ulp of 1/s for a normal s with a normal reciprocal,
+// so rc -/+ 6 ulps bracket 1/s with more than 4 ulps to spare on each side; the exact products
+// x * rc_lo and x * rc_hi then bracket fl(x / s) (which is within half an ulp of x / s), and
 // fma(x, rc_lo, M8) / fma(x, rc_hi, M8) round them to integers in one step. Equal results mean
-// every value in between, fl(x / sa) included, rounds to that integer, the rule's code (no clamp
-// is needed: |fl(x / sa)| <= 7 (1 + 2^-23) for a normal scale). Otherwise, or for a scale that is
-// 0, subnormal or above 2^126, the wave recomputes the group with the IEEE division and the clamp.
-// f = M8 + code has code + 8 in its low byte, upper nibble zero, which packs with shifts and byte
-// permutes; a final xor turns offset binary into two's complement.
-__device__ __forceinline__ void quantize16(const float (&xh)[16], float sa, uint32_t& w0, uint32_t& w1) {
-  const float rc = __builtin_amdgcn_rcpf(sa);
-  const float rlo = __uint_as_float(__float_as_uint(rc) - 6u);
-  const float rhi = __uint_as_float(__float_as_uint(rc) + 6u);
-  uint64_t bad = __ballot(!(sa >= FLT_MIN && sa <= 0x1p126f));
+// every value in between, fl(x / s) included, rounds to that integer, the rule's code (no clamp
+// is needed: |fl(x / s)| <= 7 (1 + 2^-23) for a normal scale). Otherwise, or for a scale that is
+// 0, subnormal or above 2^126, the wave recomputes both groups with the IEEE division and the
+// clamp. f = M8 + code has code + 8 in its low byte, upper nibble zero, which packs with shifts and
+// byte permutes; a final xor turns offset binary into two's complement.
+__device__ __forceinline__ void quantize8x2(const float (&xh)[16], float s0, float s1, uint32_t& w0, uint32_t& w1) {
+  const float rc0 = __builtin_amdgcn_rcpf(s0);
+  const float rc1 = __builtin_amdgcn_rcpf(s1);
+  const float rlo0 = __uint_as_float(__float_as_uint(rc0) - 6u);
+  const float rhi0 = __uint_as_float(__float_as_uint(rc0) + 6u);
+  const float rlo1 = __uint_as_float(__float_as_uint(rc1) - 6u);
+  const float rhi1 = __uint_as_float(__float_as_uint(rc1) + 6u);
+  uint64_t bad = __ballot(!(s0 >= FLT_MIN && s0 <= 0x1p126f && s1 >= FLT_MIN && s1 <= 0x1p126f));
   float f[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const float a = __builtin_fmaf(xh[e], rlo, kMagic8);
-    const float b = __builtin_fmaf(xh[e], rhi, kMagic8);
+    const float a = __builtin_fmaf(xh[e], e < 8 ? rlo0 : rlo1, kMagic8);
+    const float b = __builtin_fmaf(xh[e], e < 8 ? rhi0 : rhi1, kMagic8);
     bad |= __ballot(a != b);
     f[e] = a;
   }
   if (bad != 0ull) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
+      const float s = e < 8 ? s0 : s1;
       float q = 0.0f;
-      if (sa != 0.0f) q = fminf(fmaxf(rintf(xh[e] / sa), -8.0f), 7.0f);
+      if (s != 0.0f) q = fminf(fmaxf(rintf(xh[e] / s), -8.0f), 7.0f);
       f[e] = kMagic8 + q;
     }
   }
@@ -87,7 +100,7 @@ __device__ __forceinline__ void quantize16(const float (&xh)[16], float sa, uint
 }
 
 constexpr int kQaChunk = 6;       // groups whose loads a wave issues together
-constexpr int kTPitch = 128 + 16;  // bytes per token row of a wave's private transpose buffer
+constexpr int kTPitch = 128 + 16;  // bytes per token row of a wave's bf16 operand slice
 
 template <int NR>
 __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint16_t* __restrict__ x, int M, int K,
@@ -97,35 +110,40 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
                                                                      float* __restrict__ ascale,
                                                                      uint16_t* __restrict__ tout) {
   constexpr int kRedBytes = (NR > 0 ? NR : 1) * kWave * 16;
-  constexpr int kTBytes = kQaWaves * 16 * kTPitch;
+  constexpr int kTBytes = NR > 0 ? kQaWaves * 16 * kTPitch : 16;
   __shared__ __align__(16) uint8_t lds[kTBytes > kRedBytes ? kTBytes : kRedBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int i = lane & 15;
-  const int j = lane >> 4;
   const int m0 = blockIdx.x * 16;
-  const int m = m0 + i;
-  const bool row_ok = m < M;
   const int G = K / kGroup;
   // wave w owns the contiguous groups [g_begin, g_end)
   const int per = (G + kQaWaves - 1) / kQaWaves;
   const int g_begin = min(wave * per, G);
   const int g_end = min(g_begin + per, G);
 
-  // Loads read whole 128-byte lines: lane L brings 16 bytes (values 8(L%8) .. +7 of the group) of
-  // token L/8 (first load) and 8 + L/8 (second load); tokens past M read the last valid token.
-  // The wave's private LDS slice turns them into the compute layout (no barrier needed).
-  const uint16_t* xr0 = x + (size_t)min(m0 + (lane >> 3), M - 1) * K + 8 * (lane & 7);
-  const uint16_t* xr1 = x + (size_t)min(m0 + 8 + (lane >> 3), M - 1) * K + 8 * (lane & 7);
+  // Quantization layout: lane (rr = lane / 8, c = lane % 8) holds values 8c .. 8c+7 of a group for
+  // tokens m0 + rr (half 0) and m0 + 8 + rr (half 1): each load reads whole 128-byte lines, and
+  // the lane's 8 codes are exactly bytes 4c .. 4c+3 of the token's 32-byte code record.
+  const int rr = lane >> 3;
+  const int c = lane & 7;
+  const int mh0 = m0 + rr, mh1 = m0 + 8 + rr;
+  const bool ok0 = mh0 < M, ok1 = mh1 < M;
+  // tokens past M read the last valid token; their results are not stored
+  const uint16_t* xr0 = x + (size_t)min(mh0, M - 1) * K + 8 * c;
+  const uint16_t* xr1 = x + (size_t)min(mh1, M - 1) * K + 8 * c;
+
+  // Down-projection layout (MFMA A operand): lane (i = lane % 16, j = lane / 16) supplies token
+  // m0 + i, values 8j .. 8j+7 and 32+8j .. 32+8j+7; bf16(x_hat) reaches it through the wave's LDS
+  // slice (written in the quantization layout, read in the operand layout).
   uint8_t* tb = lds + wave * 16 * kTPitch;
-  const uint32_t tw0 = (lane >> 3) * kTPitch + 16 * (lane & 7);
+  const uint32_t tw0 = rr * kTPitch + 16 * c;
   const uint32_t tw1 = tw0 + 8 * kTPitch;
-  const uint32_t tr = i * kTPitch + 16 * j;  // + 64 for values 32 + 8j .. 32 + 8j + 7
+  const uint32_t trd = (lane & 15) * kTPitch + 16 * (lane >> 4);  // + 64 for values 32 + 8j
 
   v4f tacc[NR > 0 ? NR : 1];
 #pragma unroll
-  for (int c = 0; c < (NR > 0 ? NR : 1); ++c) tacc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < (NR > 0 ? NR : 1); ++q) tacc[q] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int gc = g_begin; gc < g_end; gc += kQaChunk) {
     // All X loads of the chunk first: they are the HBM stream of this kernel.
@@ -140,57 +158,54 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
     for (int q = 0; q < kQaChunk; ++q) {
       const int g = gc + q;
       if (g >= g_end) break;
-      const int k0 = g * kGroup + j * 8;
-      // transpose through the wave's LDS slice: lane (i, j) gets values 8j.. and 32+8j.. of token i
-      *reinterpret_cast<uint4*>(tb + tw0) = px[q][0];
-      *reinterpret_cast<uint4*>(tb + tw1) = px[q][1];
-      const uint4 p0 = *reinterpret_cast<const uint4*>(tb + tr);
-      const uint4 p1 = *reinterpret_cast<const uint4*>(tb + tr + 64);
-      const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-      float iv[16];
+      float iv[8];
       if (inv != nullptr) {
-        const float4 i00 = *reinterpret_cast<const float4*>(inv + k0);
-        const float4 i01 = *reinterpret_cast<const float4*>(inv + k0 + 4);
-        const float4 i10 = *reinterpret_cast<const float4*>(inv + k0 + 32);
-        const float4 i11 = *reinterpret_cast<const float4*>(inv + k0 + 36);
-        const float t[16] = {i00.x, i00.y, i00.z, i00.w, i01.x, i01.y, i01.z, i01.w,
-                             i10.x, i10.y, i10.z, i10.w, i11.x, i11.y, i11.z, i11.w};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) iv[e] = t[e];
+        const float4 i0 = *reinterpret_cast<const float4*>(inv + g * kGroup + 8 * c);
+        const float4 i1 = *reinterpret_cast<const float4*>(inv + g * kGroup + 8 * c + 4);
+        iv[0] = i0.x; iv[1] = i0.y; iv[2] = i0.z; iv[3] = i0.w;
+        iv[4] = i1.x; iv[5] = i1.y; iv[6] = i1.z; iv[7] = i1.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) iv[e] = 1.0f;
+        for (int e = 0; e < 8; ++e) iv[e] = 1.0f;
       }
+      const uint32_t pw[8] = {px[q][0].x, px[q][0].y, px[q][0].z, px[q][0].w,
+                              px[q][1].x, px[q][1].y, px[q][1].z, px[q][1].w};
       float xh[16];
-      float amax = 0.0f;
+      float am0 = 0.0f, am1 = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 4; ++e) {
         xh[2 * e] = bf16_lo(pw[e]) * iv[2 * e];
         xh[2 * e + 1] = bf16_hi(pw[e]) * iv[2 * e + 1];
-        amax = fmaxf(amax, fmaxf(fabsf(xh[2 * e]), fabsf(xh[2 * e + 1])));
+        xh[8 + 2 * e] = bf16_lo(pw[4 + e]) * iv[2 * e];
+        xh[9 + 2 * e] = bf16_hi(pw[4 + e]) * iv[2 * e + 1];
+        am0 = fmaxf(am0, fmaxf(fabsf(xh[2 * e]), fabsf(xh[2 * e + 1])));
+        am1 = fmaxf(am1, fmaxf(fabsf(xh[8 + 2 * e]), fabsf(xh[9 + 2 * e])));
       }
-      amax = group_max4(amax);
-      const float sa = amax / 7.0f;
+      const float s0 = div7(group_max8(am0));
+      const float s1 = div7(group_max8(am1));
       uint32_t w0, w1;
-      quantize16(xh, sa, w0, w1);
-      if (row_ok) {
-        uint8_t* qp = qact + ((size_t)g * M + m) * 32 + 4 * j;
-        *reinterpret_cast<uint32_t*>(qp) = w0;       // values 8j .. 8j+7
-        *reinterpret_cast<uint32_t*>(qp + 16) = w1;  // values 32+8j .. 32+8j+7
-        if (j == 0) ascale[(size_t)g * M + m] = sa;
+      quantize8x2(xh, s0, s1, w0, w1);
+      uint8_t* qp = qact + ((size_t)g * M + mh0) * 32 + 4 * c;
+      if (ok0) *reinterpret_cast<uint32_t*>(qp) = w0;
+      if (ok1) *reinterpret_cast<uint32_t*>(qp + 8 * 32) = w1;
+      if (c == 0) {
+        if (ok0) ascale[(size_t)g * M + mh0] = s0;
+        if (ok1) ascale[(size_t)g * M + mh1] = s1;
       }
       if constexpr (NR > 0) {
-        const uint4 a0 = {pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]), pack_bf16x2(xh[4], xh[5]),
-                          pack_bf16x2(xh[6], xh[7])};
-        const uint4 a1 = {pack_bf16x2(xh[8], xh[9]), pack_bf16x2(xh[10], xh[11]), pack_bf16x2(xh[12], xh[13]),
-                          pack_bf16x2(xh[14], xh[15])};
+        *reinterpret_cast<uint4*>(tb + tw0) = uint4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]),
+                                                    pack_bf16x2(xh[4], xh[5]), pack_bf16x2(xh[6], xh[7])};
+        *reinterpret_cast<uint4*>(tb + tw1) = uint4{pack_bf16x2(xh[8], xh[9]), pack_bf16x2(xh[10], xh[11]),
+                                                    pack_bf16x2(xh[12], xh[13]), pack_bf16x2(xh[14], xh[15])};
+        const uint4 a0 = *reinterpret_cast<const uint4*>(tb + trd);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(tb + trd + 64);
 #pragma unroll
-        for (int c = 0; c < NR; ++c) {
-          const uint16_t* bp = l1t + (((size_t)c * G + g) * 2 * kWave + lane) * 8;
+        for (int cc = 0; cc < NR; ++cc) {
+          const uint16_t* bp = l1t + (((size_t)cc * G + g) * 2 * kWave + lane) * 8;
           const uint4 b0 = *reinterpret_cast<const uint4*>(bp);
           const uint4 b1 = *reinterpret_cast<const uint4*>(bp + kWave * 8);
-          tacc[c] = mfma_bf16_16x16x32(as_v8bf(a0), as_v8bf(b0), tacc[c]);
-          tacc[c] = mfma_bf16_16x16x32(as_v8bf(a1), as_v8bf(b1), tacc[c]);
+          tacc[cc] = mfma_bf16_16x16x32(as_v8bf(a0), as_v8bf(b0), tacc[cc]);
+          tacc[cc] = mfma_bf16_16x16x32(as_v8bf(a1), as_v8bf(b1), tacc[cc]);
         }
       }
     }
@@ -198,28 +213,30 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
 
   if constexpr (NR > 0) {
     // Fixed-order reduction (((w0 + w1) + w2) + ...) + w7 of the per-wave partial T tiles.
-    __syncthreads();  // every wave is done with its transpose slice
+    const int i = lane & 15;
+    const int j = lane >> 4;
+    __syncthreads();  // every wave is done with its operand slice
     v4f* red = reinterpret_cast<v4f*>(lds);
     if (wave == 0) {
 #pragma unroll
-      for (int c = 0; c < NR; ++c) red[c * kWave + lane] = tacc[c];
+      for (int cc = 0; cc < NR; ++cc) red[cc * kWave + lane] = tacc[cc];
     }
     __syncthreads();
     for (int w = 1; w < kQaWaves; ++w) {
       if (wave == w) {
 #pragma unroll
-        for (int c = 0; c < NR; ++c) {
-          v4f s = red[c * kWave + lane];
+        for (int cc = 0; cc < NR; ++cc) {
+          v4f sum = red[cc * kWave + lane];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) s[v] = s[v] + tacc[c][v];
+          for (int v = 0; v < 4; ++v) sum[v] = sum[v] + tacc[cc][v];
           if (w < kQaWaves - 1) {
-            red[c * kWave + lane] = s;
+            red[cc * kWave + lane] = sum;
           } else {
             // MFMA C/D layout: lane (i, j), register v -> row 4j + v, column i.
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const int row = m0 + 4 * j + v;
-              if (row < M) tout[(size_t)row * r + 16 * c + i] = f32_to_bf16(s[v]);
+              if (row < M) tout[(size_t)row * r + 16 * cc + i] = f32_to_bf16(sum[v]);
             }
           }
         }
