@@ -7,7 +7,7 @@
 // float32 scales, and feeds bf16(X_hat) to bf16 MFMAs that accumulate T = X_hat L1 in float32.
 //
 // Work split: one block = 16 tokens x the whole K, 8 waves; wave w takes a contiguous eighth of the
-// groups and issues the X loads of up to 6 groups at once (the HBM stream) before computing.
+// groups; its X loads (the HBM stream) run three groups ahead of the computation.
 // Quantization works in the load layout: lane (rr = lane / 8, c = lane % 8) holds values
 // 8c..8c+7 of tokens m0 + rr and m0 + 8 + rr, so each load reads whole 128-byte lines, the group
 // absmax is a max over 8 consecutive lanes, and the lane's 8 codes are exactly bytes 4c..4c+3 of
@@ -99,7 +99,8 @@ __device__ __forceinline__ void quantize8x2(const float (&xh)[16], float s0, flo
   w1 = (lo1 | hi1) ^ 0x88888888u;
 }
 
-constexpr int kQaChunk = 6;       // groups whose loads a wave issues together
+constexpr int kQaChunk = 6;       // groups per load schedule of a wave
+constexpr int kQaAhead = 3;       // groups in flight ahead of the computation
 constexpr int kTPitch = 128 + 16;  // bytes per token row of a wave's bf16 operand slice
 
 template <int NR>
@@ -119,8 +120,8 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
   const int G = K / kGroup;
   // wave w owns the contiguous groups [g_begin, g_end)
   const int per = (G + kQaWaves - 1) / kQaWaves;
-  const int g_begin = min(wave * per, G);
-  const int g_end = min(g_begin + per, G);
+  const int g_begin = __builtin_amdgcn_readfirstlane(min(wave * per, G));
+  const int g_end = __builtin_amdgcn_readfirstlane(min(g_begin + per, G));
 
   // Quantization layout: lane (rr = lane / 8, c = lane % 8) holds values 8c .. 8c+7 of a group for
   // tokens m0 + rr (half 0) and m0 + 8 + rr (half 1): each load reads whole 128-byte lines, and
@@ -145,68 +146,87 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
 #pragma unroll
   for (int q = 0; q < (NR > 0 ? NR : 1); ++q) tacc[q] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int gc = g_begin; gc < g_end; gc += kQaChunk) {
-    // All X loads of the chunk first: they are the HBM stream of this kernel.
-    uint4 px[kQaChunk][2];
+  // One group: smoothing, absmax, scale, codes, stores and the down-projection MFMAs.
+  auto process = [&](const uint4& pa, const uint4& pb, int g) {
+    float iv[8];
+    if (inv != nullptr) {
+      const float4 i0 = *reinterpret_cast<const float4*>(inv + g * kGroup + 8 * c);
+      const float4 i1 = *reinterpret_cast<const float4*>(inv + g * kGroup + 8 * c + 4);
+      iv[0] = i0.x; iv[1] = i0.y; iv[2] = i0.z; iv[3] = i0.w;
+      iv[4] = i1.x; iv[5] = i1.y; iv[6] = i1.z; iv[7] = i1.w;
+    } else {
 #pragma unroll
-    for (int q = 0; q < kQaChunk; ++q) {
-      const int e = min(gc + q, g_end - 1) * kGroup;
-      px[q][0] = *reinterpret_cast<const uint4*>(xr0 + e);
-      px[q][1] = *reinterpret_cast<const uint4*>(xr1 + e);
+      for (int e = 0; e < 8; ++e) iv[e] = 1.0f;
     }
+    const uint32_t pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    float xh[16];
+    float am0 = 0.0f, am1 = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kQaChunk; ++q) {
-      const int g = gc + q;
-      if (g >= g_end) break;
-      float iv[8];
-      if (inv != nullptr) {
-        const float4 i0 = *reinterpret_cast<const float4*>(inv + g * kGroup + 8 * c);
-        const float4 i1 = *reinterpret_cast<const float4*>(inv + g * kGroup + 8 * c + 4);
-        iv[0] = i0.x; iv[1] = i0.y; iv[2] = i0.z; iv[3] = i0.w;
-        iv[4] = i1.x; iv[5] = i1.y; iv[6] = i1.z; iv[7] = i1.w;
-      } else {
+    for (int e = 0; e < 4; ++e) {
+      xh[2 * e] = bf16_lo(pw[e]) * iv[2 * e];
+      xh[2 * e + 1] = bf16_hi(pw[e]) * iv[2 * e + 1];
+      xh[8 + 2 * e] = bf16_lo(pw[4 + e]) * iv[2 * e];
+      xh[9 + 2 * e] = bf16_hi(pw[4 + e]) * iv[2 * e + 1];
+      am0 = fmaxf(am0, fmaxf(fabsf(xh[2 * e]), fabsf(xh[2 * e + 1])));
+      am1 = fmaxf(am1, fmaxf(fabsf(xh[8 + 2 * e]), fabsf(xh[9 + 2 * e])));
+    }
+    const float s0 = div7(group_max8(am0));
+    const float s1 = div7(group_max8(am1));
+    uint32_t w0, w1;
+    quantize8x2(xh, s0, s1, w0, w1);
+    uint8_t* qp = qact + ((size_t)g * M + mh0) * 32 + 4 * c;
+    if (ok0) *reinterpret_cast<uint32_t*>(qp) = w0;
+    if (ok1) *reinterpret_cast<uint32_t*>(qp + 8 * 32) = w1;
+    // scales: lanes c == 0 store token m0 + rr, lanes c == 1 token m0 + 8 + rr (one instruction)
+    if (c < 2 && (c == 0 ? ok0 : ok1)) ascale[(size_t)g * M + (c == 0 ? mh0 : mh1)] = c == 0 ? s0 : s1;
+    if constexpr (NR > 0) {
+      *reinterpret_cast<uint4*>(tb + tw0) = uint4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]),
+                                                  pack_bf16x2(xh[4], xh[5]), pack_bf16x2(xh[6], xh[7])};
+      *reinterpret_cast<uint4*>(tb + tw1) = uint4{pack_bf16x2(xh[8], xh[9]), pack_bf16x2(xh[10], xh[11]),
+                                                  pack_bf16x2(xh[12], xh[13]), pack_bf16x2(xh[14], xh[15])};
+      const uint4 a0 = *reinterpret_cast<const uint4*>(tb + trd);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(tb + trd + 64);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) iv[e] = 1.0f;
+      for (int cc = 0; cc < NR; ++cc) {
+        const uint16_t* bp = l1t + (((size_t)cc * G + g) * 2 * kWave + lane) * 8;
+        const uint4 b0 = *reinterpret_cast<const uint4*>(bp);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(bp + kWave * 8);
+        tacc[cc] = mfma_bf16_16x16x32(as_v8bf(a0), as_v8bf(b0), tacc[cc]);
+        tacc[cc] = mfma_bf16_16x16x32(as_v8bf(a1), as_v8bf(b1), tacc[cc]);
       }
-      const uint32_t pw[8] = {px[q][0].x, px[q][0].y, px[q][0].z, px[q][0].w,
-                              px[q][1].x, px[q][1].y, px[q][1].z, px[q][1].w};
-      float xh[16];
-      float am0 = 0.0f, am1 = 0.0f;
+    }
+  };
+
+  for (int gc = g_begin; gc < g_end; gc += kQaChunk) {
+    uint4 px[kQaChunk][2];
+    if (gc + kQaChunk <= g_end) {
+      // Full chunk: loads run kQaAhead groups ahead of the computation, so that a wave never
+      // waits to issue a load behind the whole chunk's requests while its first data is ready.
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xh[2 * e] = bf16_lo(pw[e]) * iv[2 * e];
-        xh[2 * e + 1] = bf16_hi(pw[e]) * iv[2 * e + 1];
-        xh[8 + 2 * e] = bf16_lo(pw[4 + e]) * iv[2 * e];
-        xh[9 + 2 * e] = bf16_hi(pw[4 + e]) * iv[2 * e + 1];
-        am0 = fmaxf(am0, fmaxf(fabsf(xh[2 * e]), fabsf(xh[2 * e + 1])));
-        am1 = fmaxf(am1, fmaxf(fabsf(xh[8 + 2 * e]), fabsf(xh[9 + 2 * e])));
+      for (int q = 0; q < kQaAhead; ++q) {
+        px[q][0] = *reinterpret_cast<const uint4*>(xr0 + (gc + q) * kGroup);
+        px[q][1] = *reinterpret_cast<const uint4*>(xr1 + (gc + q) * kGroup);
       }
-      const float s0 = div7(group_max8(am0));
-      const float s1 = div7(group_max8(am1));
-      uint32_t w0, w1;
-      quantize8x2(xh, s0, s1, w0, w1);
-      uint8_t* qp = qact + ((size_t)g * M + mh0) * 32 + 4 * c;
-      if (ok0) *reinterpret_cast<uint32_t*>(qp) = w0;
-      if (ok1) *reinterpret_cast<uint32_t*>(qp + 8 * 32) = w1;
-      if (c == 0) {
-        if (ok0) ascale[(size_t)g * M + mh0] = s0;
-        if (ok1) ascale[(size_t)g * M + mh1] = s1;
-      }
-      if constexpr (NR > 0) {
-        *reinterpret_cast<uint4*>(tb + tw0) = uint4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]),
-                                                    pack_bf16x2(xh[4], xh[5]), pack_bf16x2(xh[6], xh[7])};
-        *reinterpret_cast<uint4*>(tb + tw1) = uint4{pack_bf16x2(xh[8], xh[9]), pack_bf16x2(xh[10], xh[11]),
-                                                    pack_bf16x2(xh[12], xh[13]), pack_bf16x2(xh[14], xh[15])};
-        const uint4 a0 = *reinterpret_cast<const uint4*>(tb + trd);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(tb + trd + 64);
 #pragma unroll
-        for (int cc = 0; cc < NR; ++cc) {
-          const uint16_t* bp = l1t + (((size_t)cc * G + g) * 2 * kWave + lane) * 8;
-          const uint4 b0 = *reinterpret_cast<const uint4*>(bp);
-          const uint4 b1 = *reinterpret_cast<const uint4*>(bp + kWave * 8);
-          tacc[cc] = mfma_bf16_16x16x32(as_v8bf(a0), as_v8bf(b0), tacc[cc]);
-          tacc[cc] = mfma_bf16_16x16x32(as_v8bf(a1), as_v8bf(b1), tacc[cc]);
+      for (int q = 0; q < kQaChunk; ++q) {
+        if (q + kQaAhead < kQaChunk) {
+          px[q + kQaAhead][0] = *reinterpret_cast<const uint4*>(xr0 + (gc + q + kQaAhead) * kGroup);
+          px[q + kQaAhead][1] = *reinterpret_cast<const uint4*>(xr1 + (gc + q + kQaAhead) * kGroup);
         }
+        process(px[q][0], px[q][1], gc + q);
+      }
+    } else {
+      // Last, partial chunk: all its loads first (indices past the end repeat the last group).
+#pragma unroll
+      for (int q = 0; q < kQaChunk; ++q) {
+        const int e = min(gc + q, g_end - 1) * kGroup;
+        px[q][0] = *reinterpret_cast<const uint4*>(xr0 + e);
+        px[q][1] = *reinterpret_cast<const uint4*>(xr1 + e);
+      }
+#pragma unroll
+      for (int q = 0; q < kQaChunk; ++q) {
+        if (gc + q >= g_end) break;
+        process(px[q][0], px[q][1], gc + q);
       }
     }
   }
