@@ -39,6 +39,21 @@ def w4a4_problem(name: str, M: int = None, rank: int = None):
             "inv": d["inv"], "l1": d["l1_bf16"], "l2": d["l2_bf16"], "resid": d["resid"], **out}
 
 
+def random_w4a4_problem(M: int, K: int, N: int, rank: int, seed: int):
+    """A W4A4 layer of arbitrary shape from seeded N(0,1) activations (with a few outlier
+    channels), N(0, 0.02) weights and N(0, 0.01) bias, prepared and evaluated by the oracle."""
+    cfg = synth.LayerConfig(f"rand{M}x{K}x{N}", M, K, N, rank, seed=seed, n_outliers=max(1, K // 100),
+                            outlier_scale=30.0)
+    inp = synth.make_layer_inputs(cfg)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    b = synth.f32_from_bf16_bits(inp["bias"])
+    d = oracle.svdq_decompose(x, w, rank)
+    out = oracle.svdq_layer(x, d["inv"], d["l1_bf16"], d["l2_bf16"], d["resid"], b)
+    return {"cfg": cfg, "x_bits": inp["x"], "x": x, "bias_bits": inp["bias"], "bias": b,
+            "inv": d["inv"], "l1": d["l1_bf16"], "l2": d["l2_bf16"], "resid": d["resid"], **out}
+
+
 @functools.lru_cache(maxsize=4)
 def w4a16_problem(name: str = "awq", M: int = None, with_bias: bool = False):
     cfg = synth.CONFIGS[name]

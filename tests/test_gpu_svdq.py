@@ -10,7 +10,8 @@ import pytest
 
 import oracle
 import synth
-from problems import (decode_qact, tolerance_report, w4a16_problem, w4a4_problem, within_one_bf16_ulp)
+from problems import (decode_qact, random_w4a4_problem, tolerance_report, w4a16_problem, w4a4_problem,
+                      within_one_bf16_ulp)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,6 +131,25 @@ def test_w4a4_layer_parity(gpu, name, rank):
     import torch
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
     assert np.array_equal(qact.cpu().numpy(), qact2.cpu().numpy())
+
+
+# (M, K, N, rank): 1, 2, 7, 10, 16 and 50 groups (fewer groups than waves, every tail length of the
+# GEMM's six-step loop, a quantizer chunk that is full then partial), ragged M and N, ranks 0 to 112
+SMALL_SHAPES = [(33, 64, 48, 16), (130, 128, 272, 48), (77, 448, 144, 0), (200, 640, 400, 112),
+                (16, 1024, 1040, 64), (40, 3200, 160, 32)]
+
+
+@pytest.mark.parametrize("M,K,N,rank", SMALL_SHAPES, ids=[f"M{m}K{k}N{n}r{r}" for m, k, n, r in SMALL_SHAPES])
+def test_w4a4_small_shapes(gpu, M, K, N, rank):
+    import quantized_gemm_amd as q
+    say(f"[w4a4 shapes] M={M} K={K} N={N} r={rank}")
+    p = random_w4a4_problem(M, K, N, rank, seed=M + K + N + rank)
+    layer = Layer(p, gpu)
+    qact, ascale, t, y = layer.run(p["x_bits"], gpu)
+    check_activation_outputs(p, qact, ascale, t)
+    check_y(p, y)
+    got = q.svdq_debug_group_sums(qact, layer.qw, N, 0, 0, M, N).cpu().numpy()
+    assert np.array_equal(got, oracle.group_sums(p["qa"], p["qw"]))
 
 
 def test_tiny_full_group_sums(gpu):
