@@ -111,7 +111,8 @@ def svdq_pack_weights(fmt: int, w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def svdq_pack_lowrank(l1: np.ndarray, l2: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """float32 L1 [K, r], L2 [r, N] -> bf16 bits L1^T [r, K], L2^T [N, r]."""
+    """float32 L1 [K, r], L2 [r, N] -> bf16 bits of L1 in the MFMA operand-block order of
+    include/svdq.h (r*K values, shaped (r, K) for its size only) and of L2^T [N, r]."""
     l1 = np.ascontiguousarray(l1, dtype=np.float32)
     l2 = np.ascontiguousarray(l2, dtype=np.float32)
     K, r = l1.shape
