@@ -114,7 +114,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer shards by tokens or output columns with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the layer shards by tokens or output columns with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
