@@ -35,8 +35,9 @@
  *   - Every pointer must be aligned to 16 bytes. Tensors are dense and row-major.
  *   - The current device must be a gfx950 (MI355X); otherwise SVDQ_ERR_ARCH.
  *   - Inputs must be finite (NaN/Inf are outside the contract).
- *   - Shapes: 1 <= M; K % 64 == 0 and K >= 64; N % 16 == 0 and N >= 16; rank r == 0 or
- *     r % 16 == 0 with 16 <= r <= 256. All sizes < 2^31 elements per tensor.
+ *   - Shapes: 1 <= M < 2^27; K % 64 == 0 and 64 <= K < 2^31; N % 16 == 0 and 16 <= N < 2^27;
+ *     M*K, N*K and M*N below 2^40; rank r == 0 or r % 16 == 0 with 16 <= r <= 256. Other sizes
+ *     give SVDQ_ERR_SHAPE.
  *
  * Tensor formats
  *   bf16        IEEE bfloat16 stored as uint16.

@@ -14,12 +14,16 @@ std::atomic<int> g_arch_state[kMaxDevices];
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Row counts stay below 2^27 so that the kernels' 32-bit per-row byte offsets (32 bytes of codes
+// per row and group) cannot wrap; tensors stay below 2^40 elements.
+constexpr int64_t kMaxRows = int64_t(1) << 27;
+
 bool mk_ok(int64_t M, int64_t K) {
-  return M >= 1 && M < (int64_t(1) << 31) && K >= SVDQ_GROUP && K % SVDQ_GROUP == 0 && K < (int64_t(1) << 31) &&
+  return M >= 1 && M < kMaxRows && K >= SVDQ_GROUP && K % SVDQ_GROUP == 0 && K < (int64_t(1) << 31) &&
          M * K < (int64_t(1) << 40);
 }
 
-bool n_ok(int64_t N) { return N >= 16 && N % 16 == 0 && N < (int64_t(1) << 31); }
+bool n_ok(int64_t N) { return N >= 16 && N % 16 == 0 && N < kMaxRows; }
 
 bool rank_ok(int r) { return r == 0 || (r >= 16 && r <= SVDQ_MAX_RANK && r % 16 == 0); }
 

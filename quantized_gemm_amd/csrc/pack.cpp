@@ -54,7 +54,7 @@ inline int int4_code(float v, float s) {
 
 bool shape_ok(int64_t K, int64_t N) {
   return K >= SVDQ_GROUP && K % SVDQ_GROUP == 0 && N >= 16 && N % 16 == 0 && K < (int64_t(1) << 31) &&
-         N < (int64_t(1) << 31) && K * N < (int64_t(1) << 40);
+         N < (int64_t(1) << 27) && K * N < (int64_t(1) << 40);
 }
 
 // Per (group g, column n) absmax of w [K, N], scanning rows contiguously.

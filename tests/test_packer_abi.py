@@ -179,6 +179,7 @@ def test_device_entry_validation(lib):
     assert lib.svdq_quantize_act(ODD, 16, 64, None, None, 0, P, P, None, None) == -1
     assert lib.svdq_quantize_act(P, 0, 64, None, None, 0, P, P, None, None) == -2
     assert lib.svdq_quantize_act(P, 16, 96, None, None, 0, P, P, None, None) == -2
+    assert lib.svdq_quantize_act(P, 1 << 27, 64, None, None, 0, P, P, None, None) == -2   # row limit
     assert lib.svdq_quantize_act(P, 16, 64, None, P, 24, P, P, P, None) == -3
     assert lib.svdq_quantize_act(P, 16, 64, None, P, 0, P, P, None, None) == -3
     assert lib.svdq_quantize_act(P, 16, 64, None, P, 32, P, P, None, None) == -3
@@ -186,6 +187,7 @@ def test_device_entry_validation(lib):
     assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, None, None, 16, 16, 64, None) == -1
     assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, None, P, 16, 24, 64, None) == -2
     assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, None, P, 16, 16, 0, None) == -2
+    assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, None, P, 16, 1 << 27, 64, None) == -2
     assert lib.svdq_linear_w4a4(P, P, P, P, P, None, 32, None, P, 16, 16, 64, None) == -3
     assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, ODD, P, 16, 16, 64, None) == -1
     # awq_linear_w4a16(x, qw, scales, bias, y, M, N, K, stream)
