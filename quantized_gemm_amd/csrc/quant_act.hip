@@ -101,6 +101,7 @@ __device__ __forceinline__ void quantize8x2(const float (&xh)[16], float s0, flo
 
 constexpr int kQaChunk = 6;       // groups per load schedule of a wave
 constexpr int kQaAhead = 3;       // groups in flight ahead of the computation
+constexpr int kRedCols = 4;       // rank tiles of 16 columns per step of the T reduction
 constexpr int kTPitch = 128 + 16;  // bytes per token row of a wave's bf16 operand slice
 
 template <int NR>
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
                                                                      uint8_t* __restrict__ qact,
                                                                      float* __restrict__ ascale,
                                                                      uint16_t* __restrict__ tout) {
-  constexpr int kRedBytes = (NR > 0 ? NR : 1) * kWave * 16;
+  constexpr int kRedBytes = kQaWaves * kRedCols * kWave * 16;
   constexpr int kTBytes = NR > 0 ? kQaWaves * 16 * kTPitch : 16;
   __shared__ __align__(16) uint8_t lds[kTBytes > kRedBytes ? kTBytes : kRedBytes];
 
@@ -232,36 +233,37 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
   }
 
   if constexpr (NR > 0) {
-    // Fixed-order reduction (((w0 + w1) + w2) + ...) + w7 of the per-wave partial T tiles.
-    const int i = lane & 15;
-    const int j = lane >> 4;
-    __syncthreads();  // every wave is done with its operand slice
+    // T = sum of the 8 waves' partial tiles in the fixed order ((w0 + w1) + w2) + ... + w7, in
+    // chunks of up to kRedCols rank tiles: every wave parks its partials in LDS, then the 512
+    // threads each sum two elements over the 8 partials and store them as bf16.
+    // MFMA C/D layout of a partial: lane (i, j), register v -> row 4j + v, column i of the tile.
     v4f* red = reinterpret_cast<v4f*>(lds);
-    if (wave == 0) {
 #pragma unroll
-      for (int cc = 0; cc < NR; ++cc) red[cc * kWave + lane] = tacc[cc];
-    }
-    __syncthreads();
-    for (int w = 1; w < kQaWaves; ++w) {
-      if (wave == w) {
+    for (int c0 = 0; c0 < NR; c0 += kRedCols) {
+      constexpr int kChunk = NR < kRedCols ? NR : kRedCols;
+      __syncthreads();  // the operand slices / the previous chunk are no longer read
 #pragma unroll
-        for (int cc = 0; cc < NR; ++cc) {
-          v4f sum = red[cc * kWave + lane];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) sum[v] = sum[v] + tacc[cc][v];
-          if (w < kQaWaves - 1) {
-            red[cc * kWave + lane] = sum;
-          } else {
-            // MFMA C/D layout: lane (i, j), register v -> row 4j + v, column i.
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int row = m0 + 4 * j + v;
-              if (row < M) tout[(size_t)row * r + 16 * cc + i] = f32_to_bf16(sum[v]);
-            }
-          }
-        }
-      }
+      for (int cc = 0; cc < kChunk; ++cc)
+        if (c0 + cc < NR) red[(wave * kRedCols + cc) * kWave + lane] = tacc[c0 + cc];
       __syncthreads();
+      // thread -> (tile cc, lane l, registers 2h and 2h + 1)
+      const int t = threadIdx.x;
+      const int cc = (t >> 6) % kRedCols;
+      const int l = t & 63;
+      const int hv = t / (64 * kRedCols);
+      if (cc < kChunk && c0 + cc < NR && hv < 2) {
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kQaWaves; ++w) {
+          const v4f p = red[(w * kRedCols + cc) * kWave + l];
+          s0 = w == 0 ? p[2 * hv] : s0 + p[2 * hv];
+          s1 = w == 0 ? p[2 * hv + 1] : s1 + p[2 * hv + 1];
+        }
+        const int row = m0 + 4 * (l >> 4) + 2 * hv;
+        const int col = 16 * (c0 + cc) + (l & 15);
+        if (row < M) tout[(size_t)row * r + col] = f32_to_bf16(s0);
+        if (row + 1 < M) tout[(size_t)(row + 1) * r + col] = f32_to_bf16(s1);
+      }
     }
   }
 }
