@@ -59,9 +59,9 @@ __device__ __forceinline__ float div7(float a) {
 // x * rc_lo and x * rc_hi then bracket fl(x / s) (which is within half an ulp of x / s), and
 // fma(x, rc_lo, M8) / fma(x, rc_hi, M8) round them to integers in one step. Equal results mean
 // every value in between, fl(x / s) included, rounds to that integer, the rule's code (no clamp
-// is needed: |fl(x / s)| <= 7 (1 + 2^-23) for a normal scale). Otherwise, or for a scale that is
-// 0, subnormal or above 2^126, the wave recomputes both groups with the IEEE division and the
-// clamp. f = M8 + code has code + 8 in its low byte, upper nibble zero, which packs with shifts and
+// is needed: |fl(x / s)| <= 7 (1 + 2^-23) for a normal scale). Value positions where some lane
+// could not decide are recomputed with the IEEE division and the clamp; all of them when a scale
+// is 0, subnormal or above 2^126. f = M8 + code has code + 8 in its low byte, upper nibble zero, which packs with shifts and
 // byte permutes; a final xor turns offset binary into two's complement.
 __device__ __forceinline__ void quantize8x2(const float (&xh)[16], float s0, float s1, uint32_t& w0, uint32_t& w1) {
   const float rc0 = __builtin_amdgcn_rcpf(s0);
@@ -70,22 +70,29 @@ __device__ __forceinline__ void quantize8x2(const float (&xh)[16], float s0, flo
   const float rhi0 = __uint_as_float(__float_as_uint(rc0) + 6u);
   const float rlo1 = __uint_as_float(__float_as_uint(rc1) - 6u);
   const float rhi1 = __uint_as_float(__float_as_uint(rc1) + 6u);
-  uint64_t bad = __ballot(!(s0 >= FLT_MIN && s0 <= 0x1p126f && s1 >= FLT_MIN && s1 <= 0x1p126f));
+  const uint64_t scale_bad = __ballot(!(s0 >= FLT_MIN && s0 <= 0x1p126f && s1 >= FLT_MIN && s1 <= 0x1p126f));
+  uint64_t bad = scale_bad;
+  uint64_t undecided[16];  // per value position: the lanes whose bracket straddles a boundary
   float f[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const float a = __builtin_fmaf(xh[e], e < 8 ? rlo0 : rlo1, kMagic8);
     const float b = __builtin_fmaf(xh[e], e < 8 ? rhi0 : rhi1, kMagic8);
-    bad |= __ballot(a != b);
+    undecided[e] = __ballot(a != b);
+    bad |= undecided[e];
     f[e] = a;
   }
   if (bad != 0ull) {
+    // IEEE division for the positions some lane could not decide (all of them if a scale is 0,
+    // subnormal or above 2^126).
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float s = e < 8 ? s0 : s1;
-      float q = 0.0f;
-      if (s != 0.0f) q = fminf(fmaxf(rintf(xh[e] / s), -8.0f), 7.0f);
-      f[e] = kMagic8 + q;
+      if (scale_bad != 0ull || undecided[e] != 0ull) {
+        const float s = e < 8 ? s0 : s1;
+        float q = 0.0f;
+        if (s != 0.0f) q = fminf(fmaxf(rintf(xh[e] / s), -8.0f), 7.0f);
+        f[e] = kMagic8 + q;
+      }
     }
   }
   uint32_t pr[8];  // byte 0 of pr[b] = (u[2b+1] << 4) | u[2b]
