@@ -71,6 +71,12 @@ __device__ __forceinline__ uint4 unpack_chunk(uint32_t w0, uint32_t w1) {
 template <typename T>
 __device__ __forceinline__ v4i as_v4i(T u) { return __builtin_bit_cast(v4i, u); }
 
+// Raw buffer resource over `bytes` bytes at `base` (offsets past the end read zero). Row counts
+// below 2^27 keep every per-group range and lane offset within 32 bits.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // DEBUG replaces the rescale and the epilogue by a dump of the exact group sums of a window.
 template <int NR, bool DEBUG>
 __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
@@ -118,10 +124,23 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
 
   uint4 apk[2], bpk[2];
   float spk[2];
-  auto gload_a = [&](int slot, int g) { apk[slot] = *reinterpret_cast<const uint4*>(qa + (size_t)g * M * 32 + a_off); };
+  // Buffer loads: the resource holds this group's (wave-uniform) base and size in scalar registers,
+  // the lane supplies its 32-bit byte offset, so no vector instruction computes an address. The
+  // scale array is chosen per wave (threads < kBM are waves 0 and 1).
+  const bool s_is_a_w = __builtin_amdgcn_readfirstlane(tid >> 6) < kBM / kWave;
+  auto gload_a = [&](int slot, int g) {
+    apk[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              buffer_rsrc(qa + (size_t)g * M * 32, (uint32_t)M * 32u), (int)a_off, 0, 0));
+  };
   auto gload_b = [&](int slot, int g) {
-    bpk[slot] = *reinterpret_cast<const uint4*>(qw + (size_t)g * N * 32 + b_off);
-    if constexpr (!DEBUG) spk[slot] = s_is_a ? sa[(size_t)g * M + s_off] : sw[(size_t)g * N + s_off];
+    bpk[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              buffer_rsrc(qw + (size_t)g * N * 32, (uint32_t)N * 32u), (int)b_off, 0, 0));
+    if constexpr (!DEBUG) {
+      const float* base = s_is_a_w ? sa + (size_t)g * M : sw + (size_t)g * N;
+      const uint32_t bytes = s_is_a_w ? (uint32_t)M * 4u : (uint32_t)N * 4u;
+      spk[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(base, bytes),
+                                                                                   (int)(4u * s_off), 0, 0));
+    }
   };
   auto lstore = [&](int slot, uint8_t* st) {
     *reinterpret_cast<uint4*>(st + st_b) = unpack_chunk(bpk[slot].x, bpk[slot].y);
