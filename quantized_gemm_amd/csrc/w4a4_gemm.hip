@@ -328,7 +328,10 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
       const int m = m0 + row;
       const int n = n0 + c8;
       const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kEpiPitch + c8);
-      if (m < M && n < N) *reinterpret_cast<uint4*>(y + (size_t)m * N + n) = v;
+      // Y is written once and not read here: a non-temporal store keeps it from evicting the
+      // activation and weight tiles that other blocks on this XCD are still reading from L2.
+      if (m < M && n < N)
+        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i*>(y + (size_t)m * N + n));
     }
   }
 }
