@@ -18,9 +18,10 @@
 // kAwqPer consecutive groups of K (a chunk of kAwqWaves * kAwqPer groups at a time), and keeps
 // its slice of X and the 136 * Sx corrections in registers for the block's column tiles
 // t = blockIdx.x, blockIdx.x + gridDim.x, ... (up to kAwqMaxTiles per pass). The grid is about one
-// block per CU, and each wave issues the weight loads of all its tiles before computing. The partial
-// tiles of the waves are summed in LDS in a fixed order (deterministic) and wave 0 adds the bias
-// and stores bf16.
+// block per CU. Each wave keeps the weight loads of the next two tiles in flight while it computes
+// one, so the data of a CU's first tiles arrive, and are used, while the rest still streams in.
+// The partial tiles of the waves are summed in LDS in a fixed order (deterministic); wave s sums
+// tile s, adds the bias and stores bf16, so the tiles of a pass are finished in parallel.
 #include "svdq_device.h"
 #include "svdq_launch.h"
 
@@ -34,6 +35,7 @@ constexpr int kAwqMaxTiles = 5;   // column tiles accumulated per pass over K
 constexpr int kAwqBlocks = 256;   // target resident blocks (one per CU)
 
 static_assert(kAwqPer % 2 == 0, "weights are loaded in group pairs");
+static_assert(kAwqMaxTiles <= kAwqWaves, "wave s reduces tile s of a pass");
 
 __device__ __forceinline__ uint4 dequant_nibbles_bf16(uint32_t w) {
   return uint4{(w & 0x000F000Fu) | 0x43004300u, ((w >> 4) & 0x000F000Fu) | 0x43004300u,
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
   // rows past M read the last row; their results are not stored
   const uint16_t* xrow = x + (size_t)min(m0 + i, M - 1) * K;
   const uint4 ones4 = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  __shared__ v4f red[kAwqWaves - 1][kAwqMaxTiles][kWave];
+  __shared__ v4f red[kAwqWaves][kAwqMaxTiles][kWave];
 
   for (int tb = 0; tb < nts; tb += kAwqMaxTiles) {
     const int nb = min(kAwqMaxTiles, nts - tb);
@@ -108,11 +110,11 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
         xa[q][0] = *reinterpret_cast<const uint4*>(xrow + g * kGroup + 8 * j);
         xa[q][1] = *reinterpret_cast<const uint4*>(xrow + g * kGroup + 32 + 8 * j);
       }
-      // Every weight and scale load of the batch is issued before any compute: the HBM stream
-      // runs while the corrections and the first tiles are computed.
+      // The loads of the first two tiles are issued before any compute; each further tile's loads
+      // are issued when the tile two places before it is computed.
       TileLoad tl[kAwqMaxTiles];
 #pragma unroll
-      for (int s = 0; s < kAwqMaxTiles; ++s)
+      for (int s = 0; s < 2; ++s)
         if (s < nb) load_tile(tl[s], qw, scales, (int)blockIdx.x + (tb + s) * (int)gridDim.x, gb, G, N, lane, i);
       v4f corr[kAwqPer];
 #pragma unroll
@@ -125,6 +127,7 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
 #pragma unroll
       for (int s = 0; s < kAwqMaxTiles; ++s) {
         if (s >= nb) break;
+        if (s + 2 < kAwqMaxTiles && s + 2 < nb) load_tile(tl[s + 2], qw, scales, (int)blockIdx.x + (tb + s + 2) * (int)gridDim.x, gb, G, N, lane, i);
 #pragma unroll
         for (int q = 0; q < kAwqPer; ++q) {
           if (q >= ng) break;
@@ -141,30 +144,26 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
       }
     }
 
-    // Fixed-order reduction ((w0 + w1) + w2) + ... of the waves' partial tiles; wave 0 adds the
-    // bias and stores (MFMA C/D layout: lane (i, j), register v -> row 4j + v, column i).
-    if (wave > 0) {
+    // Fixed-order reduction ((w0 + w1) + w2) + ... of the waves' partial tiles; wave s reduces
+    // tile s, adds the bias and stores (MFMA C/D layout: lane (i, j), register v -> row 4j + v,
+    // column i).
 #pragma unroll
-      for (int s = 0; s < kAwqMaxTiles; ++s) red[wave - 1][s][lane] = acc[s];
-    }
+    for (int s = 0; s < kAwqMaxTiles; ++s) red[wave][s][lane] = acc[s];
     __syncthreads();
-    if (wave == 0) {
+    if (wave < nb) {
+      const int s = wave;
+      v4f a = red[0][s][lane];
+      for (int w = 1; w < kAwqWaves; ++w) {
+        const v4f p = red[w][s][lane];
 #pragma unroll
-      for (int s = 0; s < kAwqMaxTiles; ++s) {
-        if (s >= nb) break;
-        v4f a = acc[s];
-        for (int w = 1; w < kAwqWaves; ++w) {
-          const v4f p = red[w - 1][s][lane];
+        for (int v = 0; v < 4; ++v) a[v] = a[v] + p[v];
+      }
+      const int n = ((int)blockIdx.x + (tb + s) * (int)gridDim.x) * 16 + i;
+      const float b = bias != nullptr ? bf16_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) a[v] = a[v] + p[v];
-        }
-        const int n = ((int)blockIdx.x + (tb + s) * (int)gridDim.x) * 16 + i;
-        const float b = bias != nullptr ? bf16_to_f32(bias[n]) : 0.0f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = m0 + 4 * j + v;
-          if (row < M) y[(size_t)row * N + n] = f32_to_bf16(a[v] + b);
-        }
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + 4 * j + v;
+        if (row < M) y[(size_t)row * N + n] = f32_to_bf16(a[v] + b);
       }
     }
     __syncthreads();  // red is reused by the next batch of tiles
