@@ -48,7 +48,9 @@ struct TileLoad {
 };
 
 // Weights and scales of column tile t for the groups gb .. gb + kAwqPer - 1 (indices past the last
-// group are clamped to valid data; those groups are never computed).
+// group are clamped to valid data; those groups are never computed). The loaded registers are not
+// touched here: any use of a load's result makes the wave wait for it (and, loads completing in
+// order, for every load issued before it), which would hold back the loads of the next tiles.
 __device__ __forceinline__ void load_tile(TileLoad& tl, const uint8_t* __restrict__ qw,
                                           const uint16_t* __restrict__ scales, int t, int gb, int G, int N,
                                           int lane, int i) {
@@ -58,15 +60,11 @@ __device__ __forceinline__ void load_tile(TileLoad& tl, const uint8_t* __restric
   for (int p = 0; p < kAwqPer / 2; ++p) {
     const int g = min(gb + 2 * p, last_pair);
     // One 16-byte load either way. An unpaired last group holds 8 bytes per lane in a 512-byte
-    // block: lane L's bytes 8L..8L+7 lie in the aligned 16 bytes at 16*(L/2) (inside the block).
+    // block: lane L's bytes 8L..8L+7 lie in the aligned 16 bytes at 16*(L/2) (inside the block),
+    // in the upper half for odd L; the compute picks them.
     const bool paired = g + 1 < G;
     const int off = paired ? 16 * lane : 16 * (lane >> 1);
-    uint4 v = *reinterpret_cast<const uint4*>(tile + (size_t)g * 512 + off);
-    if (!paired && (lane & 1)) {
-      v.x = v.z;
-      v.y = v.w;
-    }
-    tl.w[p] = v;
+    tl.w[p] = *reinterpret_cast<const uint4*>(tile + (size_t)g * 512 + off);
   }
 #pragma unroll
   for (int q = 0; q < kAwqPer; ++q) tl.s[q] = scales[(size_t)min(gb + q, G - 1) * N + t * 16 + i];
@@ -132,8 +130,10 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
         for (int q = 0; q < kAwqPer; ++q) {
           if (q >= ng) break;
           const uint4 wp = tl[s].w[q / 2];
-          const uint32_t w0 = (q % 2 == 0) ? wp.x : wp.z;
-          const uint32_t w1 = (q % 2 == 0) ? wp.y : wp.w;
+          // an unpaired last group (only ever at an even q): odd lanes hold their codes in .z .w
+          const bool upper = (q % 2 == 1) || (gb + q + 1 >= G && (lane & 1));
+          const uint32_t w0 = upper ? wp.z : wp.x;
+          const uint32_t w1 = upper ? wp.w : wp.y;
           // the correction enters as the MFMA's C operand: d = sum x code exactly up to rounding
           v4f d = mfma_bf16_16x16x32(as_v8bf(xa[q][0]), as_v8bf(dequant_nibbles_bf16(w0)), corr[q]);
           d = mfma_bf16_16x16x32(as_v8bf(xa[q][1]), as_v8bf(dequant_nibbles_bf16(w1)), d);
