@@ -116,10 +116,13 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
   const bool s_is_a = tid < kBM;
   const uint32_t s_off = s_is_a ? (uint32_t)min(m0 + tid, M - 1) : (uint32_t)min(n0 + tid - kBM, N - 1);
   const uint32_t st_b = lrow * kPitch + 32 * lhalf;
+  // Scale slot in the stage: sa of token tid, or sw of column 32 t + c stored at 4 c + t, so that
+  // a lane reads the weight scales of its column in all four column tiles with one 16-byte read.
+  const uint32_t st_s = s_is_a ? (uint32_t)tid : (uint32_t)(kBM + ((tid - kBM) & 31) * 4 + ((tid - kBM) >> 5));
   // Operand / scale read offsets within a stage.
   const uint32_t rd_b = r32 * kPitch + 32 * h;
   const uint32_t rd_sa = kScaleOff + 4 * (wrow + 4 * h);
-  const uint32_t rd_sw = kScaleOff + 4 * (kBM + r32);
+  const uint32_t rd_sw = kScaleOff + 4 * (kBM + 4 * r32);
 
 
   uint4 apk[2], bpk[2];
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
     *reinterpret_cast<uint4*>(st + st_b) = unpack_chunk(bpk[slot].x, bpk[slot].y);
     *reinterpret_cast<uint4*>(st + st_b + 16) = unpack_chunk(bpk[slot].z, bpk[slot].w);
     if constexpr (!DEBUG) {
-      reinterpret_cast<float*>(st + kScaleOff)[tid] = spk[slot];
+      reinterpret_cast<float*>(st + kScaleOff)[st_s] = spk[slot];
     }
   };
 
@@ -192,8 +195,13 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
         sap[4 * q + 2] = f.z;
         sap[4 * q + 3] = f.w;
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) swp[t] = *reinterpret_cast<const float*>(sp + rd_sw + 4 * 32 * t);
+      {
+        const float4 f = *reinterpret_cast<const float4*>(sp + rd_sw);
+        swp[0] = f.x;
+        swp[1] = f.y;
+        swp[2] = f.z;
+        swp[3] = f.w;
+      }
     }
   };
 
@@ -248,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
       // tile 3
       __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);         // LDS read: scales
+      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);         // LDS read: scales
     }
     __syncthreads();
   };
