@@ -154,18 +154,19 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
 #pragma unroll
   for (int q = 0; q < (NR > 0 ? NR : 1); ++q) tacc[q] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // One group: smoothing, absmax, scale, codes, stores and the down-projection MFMAs.
-  auto process = [&](const uint4& pa, const uint4& pb, int g) {
-    float iv[8];
+  // Smoothing reciprocals of the lane's 8 values of group g (1 without smoothing).
+  auto load_inv = [&](int g, float4 (&iv)[2]) {
     if (inv != nullptr) {
-      const float4 i0 = *reinterpret_cast<const float4*>(inv + g * kGroup + 8 * c);
-      const float4 i1 = *reinterpret_cast<const float4*>(inv + g * kGroup + 8 * c + 4);
-      iv[0] = i0.x; iv[1] = i0.y; iv[2] = i0.z; iv[3] = i0.w;
-      iv[4] = i1.x; iv[5] = i1.y; iv[6] = i1.z; iv[7] = i1.w;
+      iv[0] = *reinterpret_cast<const float4*>(inv + g * kGroup + 8 * c);
+      iv[1] = *reinterpret_cast<const float4*>(inv + g * kGroup + 8 * c + 4);
     } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) iv[e] = 1.0f;
+      iv[0] = iv[1] = float4{1.0f, 1.0f, 1.0f, 1.0f};
     }
+  };
+
+  // One group: smoothing, absmax, scale, codes, stores and the down-projection MFMAs.
+  auto process = [&](const uint4& pa, const uint4& pb, const float4 (&ivv)[2], int g) {
+    const float iv[8] = {ivv[0].x, ivv[0].y, ivv[0].z, ivv[0].w, ivv[1].x, ivv[1].y, ivv[1].z, ivv[1].w};
     const uint32_t pw[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
     float xh[16];
     float am0 = 0.0f, am1 = 0.0f;
@@ -208,8 +209,13 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
   for (int gc = g_begin; gc < g_end; gc += kQaChunk) {
     uint4 px[kQaChunk][2];
     if (gc + kQaChunk <= g_end) {
-      // Full chunk: loads run kQaAhead groups ahead of the computation, so that a wave never
+      // Full chunk: X loads run kQaAhead groups ahead of the computation, so that a wave never
       // waits to issue a load behind the whole chunk's requests while its first data is ready.
+      // Loads complete in order, so waiting for one waits for every load issued before it: the
+      // smoothing reciprocals of group q+1 are issued before the X loads of group q+kQaAhead,
+      // and waiting for them while group q+1 is processed leaves the later X loads in flight.
+      float4 ivc[2], ivn[2];
+      load_inv(gc, ivc);
 #pragma unroll
       for (int q = 0; q < kQaAhead; ++q) {
         px[q][0] = *reinterpret_cast<const uint4*>(xr0 + (gc + q) * kGroup);
@@ -217,11 +223,15 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
       }
 #pragma unroll
       for (int q = 0; q < kQaChunk; ++q) {
+        if (q + 1 < kQaChunk) load_inv(gc + q + 1, ivn);
         if (q + kQaAhead < kQaChunk) {
           px[q + kQaAhead][0] = *reinterpret_cast<const uint4*>(xr0 + (gc + q + kQaAhead) * kGroup);
           px[q + kQaAhead][1] = *reinterpret_cast<const uint4*>(xr1 + (gc + q + kQaAhead) * kGroup);
         }
-        process(px[q][0], px[q][1], gc + q);
+        __builtin_amdgcn_sched_barrier(0);  // keep this issue order: the scheduler would sink the loads
+        process(px[q][0], px[q][1], ivc, gc + q);
+        ivc[0] = ivn[0];
+        ivc[1] = ivn[1];
       }
     } else {
       // Last, partial chunk: all its loads first (indices past the end repeat the last group).
@@ -234,7 +244,9 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
 #pragma unroll
       for (int q = 0; q < kQaChunk; ++q) {
         if (gc + q >= g_end) break;
-        process(px[q][0], px[q][1], gc + q);
+        float4 iv[2];
+        load_inv(gc + q, iv);
+        process(px[q][0], px[q][1], iv, gc + q);
       }
     }
   }
