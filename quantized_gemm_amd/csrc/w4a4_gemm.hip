@@ -233,7 +233,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
     read_scales(st);
     if constexpr (!DEBUG) {
       // Issue order: B of tile 0; A widening and its load; then per tile its rescale, the next
-      // tile's B reads and the MFMAs; the next stage's widening, LDS stores and loads; the scales.
+      // tile's B reads and the MFMAs; between tiles 1 and 2 the next stage's widening, LDS stores
+      // and loads.
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read: B tile 0
       __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU: widen A
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load: A
@@ -256,7 +257,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
       // tile 3
       __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);         // LDS read: scales
+      // (the scale reads are left to the scheduler: pinning them to the end raised the register
+      // pressure past 256 VGPRs and spilled)
     }
     __syncthreads();
   };

@@ -1,0 +1,45 @@
+"""Register budgets of the GPU kernels, as the compiler reported them in the build (no GPU needed).
+
+Every kernel is written to fit its registers without private (scratch) memory: a spill turns
+register traffic into memory traffic on the hot path, and in the W4A4 GEMM it also adds HBM writes.
+The build records the compiler's kernel-resource-usage figures next to the library; no kernel may
+use scratch, and the GEMM must keep the occupancy its design assumes (two 256-thread blocks per CU,
+i.e. two waves per SIMD).
+"""
+import os
+
+import pytest
+
+from quantized_gemm_amd import build as qbuild
+
+
+@pytest.fixture(scope="module")
+def resources():
+    if not os.path.exists(qbuild.RESOURCES):
+        pytest.fail(f"{qbuild.RESOURCES} missing: build the library first (quantized_gemm_amd/build.py)")
+    rows = []
+    for line in open(qbuild.RESOURCES):
+        if line.startswith("#") or not line.strip():
+            continue
+        src, name, vgpr, agpr, scratch, occ = line.split()
+        rows.append((src, name, int(vgpr), int(agpr), int(scratch), int(occ)))
+    return rows
+
+
+def test_every_kernel_instantiation_reported(resources):
+    count = lambda src: sum(1 for r in resources if r[0] == src)
+    # quantizer and GEMM: one instantiation per rank r = 16 q, q = 0..16 (+ the GEMM's debug dump)
+    assert count("quant_act.hip") == 17
+    assert count("w4a4_gemm.hip") == 18
+    assert count("w4a16_gemv.hip") == 1
+
+
+def test_no_kernel_uses_scratch(resources):
+    spills = [r for r in resources if r[4] != 0]
+    assert not spills, f"kernels using scratch memory: {spills}"
+
+
+def test_gemm_keeps_two_waves_per_simd(resources):
+    for r in resources:
+        if r[0] == "w4a4_gemm.hip":
+            assert r[5] >= 2, r
