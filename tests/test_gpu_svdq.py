@@ -283,10 +283,13 @@ def test_w4a16_parity(gpu, M, with_bias):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
-@pytest.mark.parametrize("M,K,N", [(20, 448, 592), (16, 6400, 96), (300, 192, 256), (3, 64, 16)])
+@pytest.mark.parametrize("M,K,N", [(20, 448, 592), (16, 6400, 96), (300, 192, 256), (3, 64, 16),
+                                   (3, 128, 24576), (2, 192, 45104)])
 def test_w4a16_shapes(gpu, M, K, N):
     """Odd group counts (unpaired last group), K longer than one chunk of the waves' slices,
-    several row tiles, column-tile counts that leave blocks with fewer tiles, the smallest shape."""
+    several row tiles, column-tile counts that leave blocks with fewer tiles, the smallest shape,
+    and more column tiles than one pass over K holds per block (N = 24576: two passes of the
+    256-block grid; N = 45104: 11 or 12 tiles per block, three passes, odd group count)."""
     import torch
     import quantized_gemm_amd as q
     say(f"[w4a16 shapes] M={M} K={K} N={N}")
