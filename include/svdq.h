@@ -167,7 +167,7 @@ int awq_linear_w4a16(const void* x, const uint8_t* qweight, const void* scales, 
 /* Parity/debug export of the exact per-group integer sums of the W4A4 product for the window
  * rows [m0, m0+tm) x columns [n0, n0+tn): out int32 [K/64, tm, tn] (out[(g*tm + i)*tn + j] =
  * P[g, m0+i, n0+j]). Uses the same kernel as svdq_linear_w4a4 with its epilogue replaced.
- * Requires 0 <= m0, m0 + tm <= M, 0 <= n0, n0 + tn <= N, tm >= 1, tn >= 1.
+ * Requires 0 <= m0, m0 + tm <= M, 0 <= n0, n0 + tn <= N, tm >= 1, tn >= 1 and (K/64)*tm*tn < 2^31.
  * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_ARCH, SVDQ_ERR_LAUNCH. */
 int svdq_debug_group_sums(const uint8_t* qact, const uint8_t* qweight, int64_t M, int64_t N, int64_t K,
                           int64_t m0, int64_t n0, int64_t tm, int64_t tn, int32_t* out, void* stream);
