@@ -14,6 +14,13 @@ Prints one JSON line. ``value`` = algorithmic operations of the step / step time
 events on the launch stream around the GEMM of every 10th timed step (every recorded event adds a
 few microseconds to its step, so the other steps carry none), against the MI355X dense int8 MFMA
 peak. The per-kernel rates of (a) and (c) are measured after the timed region, each kernel alone.
+
+``--naive-vs-fused`` instead measures the engine-design figure's panel (a) claim on this GPU (a
+rank-32 low-rank branch run naively, with a separate down projection that reads the 16-bit input
+again and a separate up projection that writes the 16-bit output again, costs 57% extra latency on
+the pages' hardware): the 4-bit branch alone (r = 0 kernels), the naive branch (r = 0 kernels plus
+torch/hipBLASLt bf16 GEMMs for X L1 and Y + T L2) and the fused kernels, and prints one JSON line
+with the three step times.
 """
 from __future__ import annotations
 
@@ -46,6 +53,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the oracle sample for this long")
     ap.add_argument("--event-every", type=int, default=10,
                     help="bracket the GEMM of every N-th timed step with HIP events")
+    ap.add_argument("--naive-vs-fused", action="store_true",
+                    help="time the 4-bit branch alone, the naive unfused low-rank branch and the fused kernels")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this size (a known-traffic "
                          "kernel that scales the HBM byte counters)")
@@ -110,12 +119,121 @@ def cpu_baseline(cfg, awq_cfg, rows: int, seconds: float):
                       f"{passes} passes, mean"}
 
 
+def naive_low_rank_layer(q, x, inv, l1s, l2, qw, sw, bias, qact, asc, y, stream=None):
+    """The unfused form of the layer (engine-design figure, panel (a)): the 4-bit branch with the
+    r = 0 kernels, a separate 16-bit down projection T = X (diag(inv) L1) that reads X again, and a
+    separate up projection Y += T L2 in place, which reads and writes the 16-bit output again
+    (torch bf16 GEMMs, float32 accumulation). l1s = bf16(diag(inv) L1) [K, r], l2 = bf16 L2 [r, N]."""
+    import torch
+    sh = None if stream is None else stream.cuda_stream
+    t = torch.matmul(x, l1s)
+    q.svdq_quantize_act(x, inv, None, qact, asc, None, stream=sh)
+    q.svdq_linear_w4a4(qact, asc, qw, sw, None, None, bias, y, stream=sh)
+    y.addmm_(t, l2)
+    return y
+
+
+def naive_vs_fused(args):
+    import torch
+    import synth
+    import quantized_gemm_amd as q
+    from quantized_gemm_amd import prep
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    q.load_library()
+    q.svdq_check_device()
+    cfg = synth.CONFIGS[args.config]
+    M, K, N, r = cfg.M, cfg.K, cfg.N, cfg.rank
+    assert r > 0, "the ablation needs a low-rank branch"
+    log(f"[ablation] generating {cfg.name} M={M} K={K} N={N} r={r}")
+    inp = synth.make_layer_inputs(cfg)
+    d = prep.decompose(synth.f32_from_bf16_bits(inp["x"]), synth.f32_from_bf16_bits(inp["w"]), r)
+    qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, d["resid"])
+    l1t, l2t = q.svdq_pack_lowrank(d["l1"], d["l2"])
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    R = max(1, args.rotate)
+    xs = [bf16_dev(inp["x"]) for _ in range(R)]
+    inv = torch.from_numpy(d["inv_smooth"]).to(dev)
+    qw_d, sw_d = torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev)
+    l1t_d, l2t_d = bf16_dev(l1t), bf16_dev(l2t)
+    l1s = torch.from_numpy(d["inv_smooth"][:, None].astype(np.float64) * d["l1"]).to(dev).to(torch.bfloat16)
+    l2 = torch.from_numpy(np.ascontiguousarray(d["l2"])).to(dev).to(torch.bfloat16)
+    bias_d = bf16_dev(inp["bias"])
+    qact = [torch.empty((K // 64, M, 32), dtype=torch.uint8, device=dev) for _ in range(R)]
+    asc = [torch.empty((K // 64, M), dtype=torch.float32, device=dev) for _ in range(R)]
+    tl = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    y0 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def four_bit(s):
+        k = s % R
+        q.svdq_quantize_act(xs[k], inv, None, qact[k], asc[k], None, stream=sh)
+        q.svdq_linear_w4a4(qact[k], asc[k], qw_d, sw_d, None, None, bias_d, y0, stream=sh)
+
+    def naive(s):
+        k = s % R
+        naive_low_rank_layer(q, xs[k], inv, l1s, l2, qw_d, sw_d, bias_d, qact[k], asc[k], y, stream)
+
+    def fused(s):
+        k = s % R
+        q.svdq_quantize_act(xs[k], inv, l1t_d, qact[k], asc[k], tl[k], stream=sh)
+        q.svdq_linear_w4a4(qact[k], asc[k], qw_d, sw_d, tl[k], l2t_d, bias_d, y, stream=sh)
+
+    def down_only(s):
+        torch.matmul(xs[s % R], l1s)
+
+    def up_only(s):
+        y.addmm_(tl[s % R], l2)
+
+    def timed(fn, n):
+        for s in range(min(n, 20)):
+            fn(s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for s in range(n):
+            fn(s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    n = max(1, args.steps)
+    res = {}
+    for name, fn in (("four_bit_only_us", four_bit), ("naive_us", naive), ("fused_us", fused),
+                     ("down_projection_torch_us", down_only), ("up_projection_torch_us", up_only)):
+        log(f"[ablation] {name}")
+        res[name] = round(timed(fn, n), 2)
+    out = {
+        "metric": f"latency of the rank-{r} low-rank branch, naive (separate 16-bit down and up projections) "
+                  f"vs fused ({cfg.name} M{M} K{K} N{N})",
+        "unit": "us",
+        "steps": n,
+        "config": {"workload": f"svdq_w4a4 {cfg.name} M{M} K{K} N{N} r{r}", "rotating_buffer_sets": R},
+        **res,
+        "naive_overhead": round(res["naive_us"] / res["four_bit_only_us"] - 1.0, 4),
+        "fused_overhead": round(res["fused_us"] / res["four_bit_only_us"] - 1.0, 4),
+        "pages_naive_overhead": 0.57,
+        "pages_context": "engine-design figure (a) of the Nunchaku README, NVIDIA GPU, rank 32",
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer shards by tokens or output columns with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
+
+    if args.naive_vs_fused:
+        naive_vs_fused(args)
+        return
 
     import torch
     import synth

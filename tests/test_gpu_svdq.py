@@ -305,3 +305,38 @@ def test_w4a16_shapes(gpu, M, K, N):
     mx, mean = tolerance_report(bf16_to_np(y), y_ref)
     say(f"  Y max|err|/max|Y| = {mx:.3e}, mean rel = {mean:.3e}")
     assert mx <= MAX_REL and mean <= MEAN_REL
+
+
+# ---------------------------------------------------------------------------------------------
+# the unfused form timed by bench.py --naive-vs-fused computes the same layer
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "attn"])
+def test_naive_unfused_layer_matches_oracle(gpu, name):
+    """bench.py's naive form (r = 0 kernels + separate bf16 down / up projections) against the
+    oracle. It is not the product path, and it has two more bf16 roundings than the fused kernels:
+    diag(inv) L1 is rounded to bf16 (the down projection reads X itself), and the 4-bit branch's
+    output is rounded to bf16 before T L2 is added (the extra 16-bit write the engine-design
+    figure describes). Each adds at most 2^-9 relative error per term, so the mean relative bar
+    for this form is 2e-3 + 2 * 2^-9; the max bar is the product's."""
+    import torch
+    import quantized_gemm_amd as q
+    import bench
+    say(f"[naive layer] {name}")
+    p = w4a4_problem(name)
+    M, K = p["x"].shape
+    N = p["resid"].shape[1]
+    qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, p["resid"])
+    l1s = to_dev(p["inv"][:, None].astype(np.float64) * p["l1"], gpu).to(torch.bfloat16)
+    l2 = to_dev(np.ascontiguousarray(p["l2"]), gpu).to(torch.bfloat16)
+    x = to_dev_bf16(p["x_bits"], gpu)
+    qact = torch.empty((K // 64, M, 32), dtype=torch.uint8, device=gpu)
+    asc = torch.empty((K // 64, M), dtype=torch.float32, device=gpu)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=gpu)
+    bias = None if p["bias_bits"] is None else to_dev_bf16(p["bias_bits"], gpu)
+    bench.naive_low_rank_layer(q, x, to_dev(p["inv"], gpu), l1s, l2, to_dev(qw, gpu), to_dev(sw, gpu), bias,
+                               qact, asc, y)
+    torch.cuda.synchronize()
+    mx, mean = tolerance_report(bf16_to_np(y), p["y"])
+    say(f"  Y max|err|/max|Y| = {mx:.3e}, mean rel = {mean:.3e}")
+    assert mx <= MAX_REL and mean <= MEAN_REL + 2 * 2.0 ** -9
+
