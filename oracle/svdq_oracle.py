@@ -32,6 +32,11 @@ bf16(X_hat) and its result T is stored as bf16; the output is rounded to bf16. T
 is bf16(float32(absmax)/7) and its codes are computed against that rounded scale.
 The main product is evaluated in float64 (the exact integer group sums times the float32
 scales), the smoothing/SVD preparation in float64.
+
+* The same Diffusers blog ("From SVDQuant to Nunchaku Lite") names a dedicated GELU/MLP execution
+  path of the Nunchaku engine. The pages give no formula; the reading here is the tanh form of
+  GELU used by FLUX-style MLPs, applied to the layer's unrounded output before the bf16 rounding:
+  Y = bf16( gelu_tanh(Y_pre) ), gelu_tanh(v) = v/2 (1 + tanh( sqrt(2/pi) (v + 0.044715 v^3) )).
 """
 from __future__ import annotations
 
@@ -44,7 +49,7 @@ __all__ = [
     "GROUP", "bf16_round", "smoothing_factors", "svdq_decompose", "int4_quantize_rows",
     "quantize_weights_w4a4", "smooth_activations", "quantize_activations", "lowrank_down",
     "group_sums", "dequant_product", "svdq_linear", "svdq_layer", "quantize_weights_w4a16",
-    "awq_linear",
+    "awq_linear", "gelu_tanh", "svdq_linear_gelu",
 ]
 
 
@@ -196,6 +201,20 @@ def svdq_linear(qa, sa, qw, sw, t=None, l2_bf16=None, bias=None):
     if bias is not None:
         y = y + bias.astype(np.float64)[None, :]
     return y, bf16_round(y.astype(np.float32))
+
+
+def gelu_tanh(v) -> np.ndarray:
+    """GELU in its tanh form, in float64: v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))."""
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * v * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (v + 0.044715 * v ** 3)))
+
+
+def svdq_linear_gelu(qa, sa, qw, sw, t=None, l2_bf16=None, bias=None):
+    """The up projection of an MLP with its activation: Y = bf16( gelu_tanh(Y_pre) ), Y_pre the
+    float64 layer output of svdq_linear. Returns (float64 gelu(Y_pre), bf16-rounded float32)."""
+    y_pre, _ = svdq_linear(qa, sa, qw, sw, t, l2_bf16, bias)
+    g = gelu_tanh(y_pre)
+    return g, bf16_round(g.astype(np.float32))
 
 
 def svdq_layer(x, inv, l1_bf16, l2_bf16, resid, bias=None):

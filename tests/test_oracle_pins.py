@@ -411,3 +411,43 @@ def test_awq_linear_triple_loop():
                 acc += float(x[m, k]) * float(codes[k, n]) * float(s[k // 64, n])
             assert abs(y64[m, n] - acc) <= 1e-12 * max(1.0, abs(acc))
             assert y[m, n] == bf16_nearest_by_definition(f32(y64[m, n]))
+
+
+# ---------------------------------------------------------------------------------------------
+# GELU (tanh form) of the MLP path
+# ---------------------------------------------------------------------------------------------
+def test_gelu_tanh_against_library_and_identities():
+    """Pinned to torch's tanh-form GELU in float64 (CPU), to the identity gelu(x) - gelu(-x) = x
+    of this form, to gelu'(0) = 1/2, to its limits, and to the tabulated gelu_tanh(1)."""
+    import torch
+    x = np.concatenate([np.linspace(-12.0, 12.0, 2401), [0.0, 1e-30, -1e-30, 1e6, -1e6]])
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    got = oracle.gelu_tanh(x)
+    # absolute agreement: in the negative tail 1 + tanh(u) cancels in both implementations
+    assert np.all(np.abs(got - ref) <= 1e-15 * np.maximum(1.0, np.abs(x)))
+    assert np.allclose(oracle.gelu_tanh(x) - oracle.gelu_tanh(-x), x, rtol=1e-12, atol=1e-12)
+    h = 1e-6
+    assert abs((oracle.gelu_tanh(h) - oracle.gelu_tanh(-h)) / (2 * h) - 0.5) < 1e-9
+    assert oracle.gelu_tanh(0.0) == 0.0
+    assert oracle.gelu_tanh(40.0) == 40.0 and oracle.gelu_tanh(-40.0) == 0.0
+    assert abs(float(oracle.gelu_tanh(1.0)) - 0.8411919906082768) < 1e-15
+
+
+def test_svdq_linear_gelu_is_gelu_of_the_layer():
+    """The MLP form applies the activation to the unrounded layer output, then rounds to bf16
+    (checked through torch's GELU on the layer's float64 output)."""
+    import torch
+    cfg = synth.CONFIGS["tiny"]
+    inp = synth.make_layer_inputs(cfg)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    b = synth.f32_from_bf16_bits(inp["bias"])
+    d = oracle.svdq_decompose(x, w, cfg.rank)
+    out = oracle.svdq_layer(x, d["inv"], d["l1_bf16"], d["l2_bf16"], d["resid"], b)
+    g64, g = oracle.svdq_linear_gelu(out["qa"], out["sa"], out["qw"], out["sw"], out["t"], d["l2_bf16"], b)
+    ref = torch.nn.functional.gelu(torch.from_numpy(out["y64"]), approximate="tanh").numpy()
+    assert np.all(np.abs(g64 - ref) <= 1e-15 * np.maximum(1.0, np.abs(out["y64"])))
+    gr = oracle.bf16_round(ref.astype(np.float32))
+    assert np.mean(g == gr) > 0.999 and np.all(np.abs(g - gr) <= 2.0 ** -8 * np.abs(gr) + 1e-30)
+    # negative pre-activations shrink towards 0, positive ones stay close to themselves
+    assert np.all(np.abs(g64) <= np.abs(out["y64"]) + 1e-12)
