@@ -158,6 +158,16 @@ int svdq_linear_w4a4(const uint8_t* qact, const float* ascale, const uint8_t* qw
                      const void* lora_act, const void* l2t, int r, const void* bias, void* y,
                      int64_t M, int64_t N, int64_t K, void* stream);
 
+/* The same layer with the MLP activation fused into its epilogue (the GELU/MLP execution path that
+ * the Diffusers blog on Nunchaku Lite names, "From SVDQuant to Nunchaku Lite"; the tanh form of GELU,
+ * a reading: the pages give no formula):
+ *   Y = bf16( gelu(Y_pre) ),  gelu(v) = v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))),
+ * Y_pre the unrounded output of svdq_linear_w4a4. For the up projection of an MLP, whose output
+ * feeds the next layer's svdq_quantize_act. Arguments, layouts and errors as svdq_linear_w4a4. */
+int svdq_linear_w4a4_gelu(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                          const void* lora_act, const void* l2t, int r, const void* bias, void* y,
+                          int64_t M, int64_t N, int64_t K, void* stream);
+
 /* W4A16 projection (awq_w4a16 layers of the Diffusers blog): Y = bf16( X dequant(qweight, scales) + b ),
  * X bf16 [M, K], packed weights in the W4A16 block layout, scales bf16 [K/64, N], bias bf16 [N] or NULL.
  * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_ARCH, SVDQ_ERR_LAUNCH. */

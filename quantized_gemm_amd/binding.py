@@ -34,6 +34,7 @@ _SIGNATURES = {
     "svdq_pack_lowrank": (_int, [_vp, _vp, _i64, _i64, _int, _vp, _vp]),
     "svdq_quantize_act": (_int, [_vp, _i64, _i64, _vp, _vp, _int, _vp, _vp, _vp, _vp]),
     "svdq_linear_w4a4": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "svdq_linear_w4a4_gelu": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _vp]),
     "awq_linear_w4a16": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "svdq_debug_group_sums": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp]),
 }
@@ -183,9 +184,13 @@ def svdq_quantize_act(x, inv_smooth, l1t, qact=None, ascale=None, lora_act=None,
     return qact, ascale, (lora_act if r else None)
 
 
-def svdq_linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, bias, y=None, stream=None):
+def svdq_linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, bias, y=None, stream=None, activation=None):
     """Kernel (b). qact uint8 [K/64, M, 32] (group-major codes), ascale float32 [K/64, M],
-    qweight uint8 (K*N/2 bytes, group-major), wscale float32 [K/64, N]. Returns y bf16 [M, N]."""
+    qweight uint8 (K*N/2 bytes, group-major), wscale float32 [K/64, N]. Returns y bf16 [M, N].
+    activation: None, or "gelu_tanh" for the MLP up projection (svdq_linear_w4a4_gelu)."""
+    if activation not in (None, "gelu_tanh"):
+        raise ValueError(f"unknown activation {activation!r}")
+    fn = "svdq_linear_w4a4" if activation is None else "svdq_linear_w4a4_gelu"
     import torch
     G, M = ascale.shape
     K = G * GROUP
@@ -197,13 +202,13 @@ def svdq_linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, bias, y=None,
         raise ValueError("qweight size does not match [N, K/2]")
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=qact.device)
-    st = load_library().svdq_linear_w4a4(
+    st = getattr(load_library(), fn)(
         _dev_ptr(qact, "qact", (torch.uint8,)), _dev_ptr(ascale, "ascale", (torch.float32,), (K // GROUP, M)),
         _dev_ptr(qweight, "qweight", (torch.uint8,)), _dev_ptr(wscale, "wscale", (torch.float32,), (K // GROUP, N)),
         _dev_ptr(lora_act, "lora_act", _bf16(), (M, r)) if r else None,
         _dev_ptr(l2t, "l2t", _bf16(), (N, r)) if r else None, r,
         _dev_ptr(bias, "bias", _bf16(), (N,)), _dev_ptr(y, "y", _bf16(), (M, N)), M, N, K, _stream(stream))
-    _check("svdq_linear_w4a4", st)
+    _check(fn, st)
     return y
 
 

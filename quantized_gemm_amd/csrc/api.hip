@@ -50,6 +50,25 @@ int device_status() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_LAUNCH; }
 
+int linear_w4a4(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                const void* lora_act, const void* l2t, int r, const void* bias, void* y, int64_t M, int64_t N,
+                int64_t K, bool gelu, void* stream) {
+  if (qact == nullptr || ascale == nullptr || qweight == nullptr || wscale == nullptr || y == nullptr)
+    return SVDQ_ERR_NULL;
+  if (!aligned16(qact) || !aligned16(ascale) || !aligned16(qweight) || !aligned16(wscale) || !aligned16(y) ||
+      (lora_act && !aligned16(lora_act)) || (l2t && !aligned16(l2t)) || (bias && !aligned16(bias)))
+    return SVDQ_ERR_NULL;
+  if (!mk_ok(M, K) || !n_ok(N) || N * K >= (int64_t(1) << 40) || M * N >= (int64_t(1) << 40)) return SVDQ_ERR_SHAPE;
+  if (!rank_ok(r)) return SVDQ_ERR_RANK;
+  if ((r == 0) != (lora_act == nullptr) || (r == 0) != (l2t == nullptr)) return SVDQ_ERR_RANK;
+  const int st = device_status();
+  if (st != SVDQ_OK) return st;
+  return launch_status(svdq::launch_w4a4_gemm(qact, ascale, qweight, wscale, static_cast<const uint16_t*>(lora_act),
+                                              static_cast<const uint16_t*>(l2t), r,
+                                              static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), (int)M,
+                                              (int)N, (int)K, gelu, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -91,20 +110,13 @@ int svdq_quantize_act(const void* x, int64_t M, int64_t K, const float* inv_smoo
 int svdq_linear_w4a4(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                      const void* lora_act, const void* l2t, int r, const void* bias, void* y, int64_t M, int64_t N,
                      int64_t K, void* stream) {
-  if (qact == nullptr || ascale == nullptr || qweight == nullptr || wscale == nullptr || y == nullptr)
-    return SVDQ_ERR_NULL;
-  if (!aligned16(qact) || !aligned16(ascale) || !aligned16(qweight) || !aligned16(wscale) || !aligned16(y) ||
-      (lora_act && !aligned16(lora_act)) || (l2t && !aligned16(l2t)) || (bias && !aligned16(bias)))
-    return SVDQ_ERR_NULL;
-  if (!mk_ok(M, K) || !n_ok(N) || N * K >= (int64_t(1) << 40) || M * N >= (int64_t(1) << 40)) return SVDQ_ERR_SHAPE;
-  if (!rank_ok(r)) return SVDQ_ERR_RANK;
-  if ((r == 0) != (lora_act == nullptr) || (r == 0) != (l2t == nullptr)) return SVDQ_ERR_RANK;
-  const int st = device_status();
-  if (st != SVDQ_OK) return st;
-  return launch_status(svdq::launch_w4a4_gemm(qact, ascale, qweight, wscale, static_cast<const uint16_t*>(lora_act),
-                                              static_cast<const uint16_t*>(l2t), r,
-                                              static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), (int)M,
-                                              (int)N, (int)K, static_cast<hipStream_t>(stream)));
+  return linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, r, bias, y, M, N, K, false, stream);
+}
+
+int svdq_linear_w4a4_gelu(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                          const void* lora_act, const void* l2t, int r, const void* bias, void* y, int64_t M,
+                          int64_t N, int64_t K, void* stream) {
+  return linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, r, bias, y, M, N, K, true, stream);
 }
 
 int awq_linear_w4a16(const void* x, const uint8_t* qweight, const void* scales, const void* bias, void* y, int64_t M,

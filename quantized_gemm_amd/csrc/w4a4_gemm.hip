@@ -61,6 +61,18 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
   tn = (t % width) / gsz;
 }
 
+// GELU in its tanh form (the GELU/MLP path named in the Diffusers blog on Nunchaku Lite), through
+// the logistic identity (1 + tanh(u)) / 2 = 1 / (1 + e^(-2u)):
+//     gelu(x) = x / (1 + 2^(-2 log2(e) u)),   u = sqrt(2/pi) (x + 0.044715 x^3),
+// with the hardware exp2 and reciprocal (each within about an ulp; no cancellation for negative
+// x, and the limits come out exactly: x -> -inf gives -0, x -> +inf gives x).
+__device__ __forceinline__ float gelu_tanh(float x) {
+  constexpr float kC = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float u = x * __builtin_fmaf(0.044715f, x * x, 1.0f);
+  const float e = __builtin_amdgcn_exp2f(kC * u);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 __device__ __forceinline__ uint4 unpack_chunk(uint32_t w0, uint32_t w1) {
   int o0, e0, o1, e1;
   unpack_nibbles_x16(w0, o0, e0);
@@ -83,7 +95,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qw,
     const float* __restrict__ sw, const uint16_t* __restrict__ tlr, const uint16_t* __restrict__ l2t, int r,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n,
-    int32_t* __restrict__ dbg, int dm0, int dn0, int dtm, int dtn) {
+    int gelu, int32_t* __restrict__ dbg, int dm0, int dn0, int dtm, int dtn) {
   __shared__ __align__(16) uint8_t lds[kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -326,8 +338,11 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
       const int n = n0 + 32 * t + r32;
       const float bv = (bias != nullptr && n < N) ? bf16_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        tile[(wrow + 8 * (v >> 2) + 4 * h + (v & 3)) * kEpiPitch + 32 * t + r32] = f32_to_bf16(acc[t][v] + bv);
+      for (int v = 0; v < 16; ++v) {
+        float o = acc[t][v] + bv;
+        if (gelu) o = gelu_tanh(o);
+        tile[(wrow + 8 * (v >> 2) + 4 * h + (v & 3)) * kEpiPitch + 32 * t + r32] = f32_to_bf16(o);
+      }
     }
     __syncthreads();
     // 128 rows x 256 bytes: thread -> (row = 16 * pass + tid / 16, 16-byte chunk tid % 16)
@@ -348,12 +363,12 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
 
 template <int NR>
 hipError_t launch_nr(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw, const uint16_t* t,
-                     const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y, int M, int N, int K,
+                     const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y, int M, int N, int K, bool gelu,
                      hipStream_t stream) {
   const int tiles_m = (M + kBM - 1) / kBM;
   const int tiles_n = (N + kBN - 1) / kBN;
   hipLaunchKernelGGL((w4a4_gemm_kernel<NR, false>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, qa, sa, qw,
-                     sw, t, l2t, r, bias, y, M, N, K, tiles_m, tiles_n, nullptr, 0, 0, 0, 0);
+                     sw, t, l2t, r, bias, y, M, N, K, tiles_m, tiles_n, gelu ? 1 : 0, nullptr, 0, 0, 0, 0);
   return hipGetLastError();
 }
 
@@ -361,25 +376,25 @@ hipError_t launch_nr(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
 
 hipError_t launch_w4a4_gemm(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                             const uint16_t* t, const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y,
-                            int M, int N, int K, hipStream_t stream) {
+                            int M, int N, int K, bool gelu, hipStream_t stream) {
   switch (r / 16) {
-    case 0: return launch_nr<0>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 1: return launch_nr<1>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 2: return launch_nr<2>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 3: return launch_nr<3>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 4: return launch_nr<4>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 5: return launch_nr<5>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 6: return launch_nr<6>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 7: return launch_nr<7>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 8: return launch_nr<8>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 9: return launch_nr<9>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 10: return launch_nr<10>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 11: return launch_nr<11>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 12: return launch_nr<12>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 13: return launch_nr<13>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 14: return launch_nr<14>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 15: return launch_nr<15>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
-    case 16: return launch_nr<16>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, stream);
+    case 0: return launch_nr<0>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 1: return launch_nr<1>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 2: return launch_nr<2>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 3: return launch_nr<3>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 4: return launch_nr<4>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 5: return launch_nr<5>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 6: return launch_nr<6>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 7: return launch_nr<7>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 8: return launch_nr<8>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 9: return launch_nr<9>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 10: return launch_nr<10>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 11: return launch_nr<11>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 12: return launch_nr<12>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 13: return launch_nr<13>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 14: return launch_nr<14>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 15: return launch_nr<15>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 16: return launch_nr<16>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -390,7 +405,7 @@ hipError_t launch_w4a4_group_sums(const uint8_t* qact, const uint8_t* qweight, i
   const int tn0 = n0 / kBN, tn1 = (n0 + tn - 1) / kBN;
   const dim3 grid(tn1 - tn0 + 1, tm1 - tm0 + 1);
   hipLaunchKernelGGL((w4a4_gemm_kernel<0, true>), grid, dim3(kThreads), 0, stream, qact, nullptr, qweight, nullptr,
-                     nullptr, nullptr, 0, nullptr, nullptr, M, N, K, 0, 0, out, m0, n0, tm, tn);
+                     nullptr, nullptr, 0, nullptr, nullptr, M, N, K, 0, 0, 0, out, m0, n0, tm, tn);
   return hipGetLastError();
 }
 

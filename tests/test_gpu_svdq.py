@@ -262,6 +262,66 @@ def test_no_smoothing_pointer(gpu):
 
 
 # ---------------------------------------------------------------------------------------------
+# MLP up projection with the GELU fused into the epilogue
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["tiny", "up"])
+def test_w4a4_gelu_parity(gpu, name):
+    import torch
+    import quantized_gemm_amd as q
+    say(f"[w4a4 gelu parity] {name}: building oracle problem")
+    p = w4a4_problem(name)
+    layer = Layer(p, gpu)
+    x = to_dev_bf16(p["x_bits"], gpu)
+    qact, ascale, t = q.svdq_quantize_act(x, layer.inv, layer.l1t)
+    y = q.svdq_linear_w4a4(qact, ascale, layer.qw, layer.sw, t, layer.l2t, layer.bias, activation="gelu_tanh")
+    y_plain = q.svdq_linear_w4a4(qact, ascale, layer.qw, layer.sw, t, layer.l2t, layer.bias)
+    torch.cuda.synchronize()
+    _, y_ref = oracle.svdq_linear_gelu(p["qa"], p["sa"], p["qw"], p["sw"], p["t"], p["l2"], p["bias"])
+    mx, mean = tolerance_report(bf16_to_np(y), y_ref)
+    say(f"  GELU(Y) max|err|/max|Y| = {mx:.3e}, mean rel = {mean:.3e}")
+    assert mx <= MAX_REL and mean <= MEAN_REL
+    # the plain entry point is unchanged by the flag
+    check_y(p, y_plain)
+
+
+def test_mlp_pair_chained_on_real_intermediates(gpu):
+    """Up projection with the fused GELU, then the down projection quantizing that output: the
+    intermediate against the oracle's, and the down layer bit-exact (codes, scales) and within
+    tolerance (Y) against the oracle run on the intermediate the GPU produced."""
+    import torch
+    import quantized_gemm_amd as q
+    M, D, F, r = 256, 256, 512, 16
+    say(f"[mlp pair] M={M} D={D} F={F} r={r}")
+    up = random_w4a4_problem(M, D, F, r, seed=71)
+    h_ref64, h_ref = oracle.svdq_linear_gelu(up["qa"], up["sa"], up["qw"], up["sw"], up["t"], up["l2"], up["bias"])
+    # the down layer, prepared from the oracle's intermediate (its smoothing needs activation maxima)
+    w_dn = synth.random_f32((F, D), seed=72, scale=0.02)
+    b_dn = oracle.bf16_round(synth.random_f32((D,), seed=73, scale=0.01))
+    d_dn = oracle.svdq_decompose(h_ref, w_dn, r)
+    upl = Layer(up, gpu)
+    x = to_dev_bf16(up["x_bits"], gpu)
+    qa1, sa1, t1 = q.svdq_quantize_act(x, upl.inv, upl.l1t)
+    h = q.svdq_linear_w4a4(qa1, sa1, upl.qw, upl.sw, t1, upl.l2t, upl.bias, activation="gelu_tanh")
+    qw2, sw2 = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, d_dn["resid"])
+    l1t2, l2t2 = q.svdq_pack_lowrank(d_dn["l1_bf16"], d_dn["l2_bf16"])
+    qa2, sa2, t2 = q.svdq_quantize_act(h, to_dev(d_dn["inv"], gpu), to_dev_bf16(l1t2, gpu))
+    y = q.svdq_linear_w4a4(qa2, sa2, to_dev(qw2, gpu), to_dev(sw2, gpu), t2, to_dev_bf16(l2t2, gpu),
+                           to_dev_bf16(synth.bf16_bits_from_f32(b_dn), gpu))
+    torch.cuda.synchronize()
+    h_gpu = bf16_to_np(h)
+    mx, mean = tolerance_report(h_gpu, h_ref)
+    say(f"  H = GELU(up) max|err|/max|H| = {mx:.3e}, mean rel = {mean:.3e}")
+    assert mx <= MAX_REL and mean <= MEAN_REL
+    dn = oracle.svdq_layer(h_gpu, d_dn["inv"], d_dn["l1_bf16"], d_dn["l2_bf16"], d_dn["resid"], b_dn)
+    assert np.array_equal(decode_qact(qa2.cpu().numpy(), M, F), dn["qa"]), "down-layer codes differ"
+    assert np.array_equal(sa2.cpu().numpy().view(np.uint32), np.ascontiguousarray(dn["sa"]).view(np.uint32))
+    mx, mean = tolerance_report(bf16_to_np(y), dn["y"])
+    say(f"  Y = down(H) max|err|/max|Y| = {mx:.3e}, mean rel = {mean:.3e}")
+    assert mx <= MAX_REL and mean <= MEAN_REL
+
+
+# ---------------------------------------------------------------------------------------------
 # W4A16 projection
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("M,with_bias", [(16, False), (16, True), (1, False), (5, True), (33, False)])
