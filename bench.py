@@ -21,6 +21,11 @@ again and a separate up projection that writes the 16-bit output again, costs 57
 the pages' hardware): the 4-bit branch alone (r = 0 kernels), the naive branch (r = 0 kernels plus
 torch/hipBLASLt bf16 GEMMs for X L1 and Y + T L2) and the fused kernels, and prints one JSON line
 with the three step times.
+
+``--mlp-pair`` times the FLUX MLP pair chained on real intermediates: the up projection (M4608,
+3072 -> 12288, r32) with the tanh-form GELU fused into its epilogue, then the down projection
+(12288 -> 3072, r32) quantizing that output. It compares the same chain with the GELU run as a
+separate bf16 pass (torch) between the two layers, and prints one JSON line.
 """
 from __future__ import annotations
 
@@ -55,6 +60,8 @@ def parse():
                     help="bracket the GEMM of every N-th timed step with HIP events")
     ap.add_argument("--naive-vs-fused", action="store_true",
                     help="time the 4-bit branch alone, the naive unfused low-rank branch and the fused kernels")
+    ap.add_argument("--mlp-pair", action="store_true",
+                    help="time the up (+GELU) -> down MLP pair, GELU fused vs a separate GELU pass")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this size (a known-traffic "
                          "kernel that scales the HBM byte counters)")
@@ -224,6 +231,102 @@ def naive_vs_fused(args):
     print(json.dumps(out), flush=True)
 
 
+def mlp_pair(args):
+    import torch
+    import synth
+    import quantized_gemm_amd as q
+    from quantized_gemm_amd import prep
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    q.load_library()
+    q.svdq_check_device()
+    cu, cd = synth.CONFIGS["up"], synth.CONFIGS["down"]
+    M, D, F = cu.M, cu.K, cu.N
+    assert cd.K == F and cd.N == D and cd.M == M
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def layer(cfg):
+        inp = synth.make_layer_inputs(cfg)
+        d = prep.decompose(synth.f32_from_bf16_bits(inp["x"]), synth.f32_from_bf16_bits(inp["w"]), cfg.rank)
+        qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, d["resid"])
+        l1t, l2t = q.svdq_pack_lowrank(d["l1"], d["l2"])
+        return inp, {"inv": torch.from_numpy(d["inv_smooth"]).to(dev), "qw": torch.from_numpy(qw).to(dev),
+                     "sw": torch.from_numpy(sw).to(dev), "l1t": bf16_dev(l1t), "l2t": bf16_dev(l2t),
+                     "bias": bf16_dev(inp["bias"]), "r": cfg.rank, "K": cfg.K}
+
+    log("[mlp pair] preparing the up and down layers")
+    inp_u, up = layer(cu)
+    _, dn = layer(cd)
+    R = max(1, args.rotate)
+    xs = [bf16_dev(inp_u["x"]) for _ in range(R)]
+
+    def bufs(L, rows):
+        return (torch.empty((L["K"] // 64, rows, 32), dtype=torch.uint8, device=dev),
+                torch.empty((L["K"] // 64, rows), dtype=torch.float32, device=dev),
+                torch.empty((rows, L["r"]), dtype=torch.bfloat16, device=dev))
+    bu, bd = bufs(up, M), bufs(dn, M)
+    h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def run(L, b, xin, out, act=None):
+        q.svdq_quantize_act(xin, L["inv"], L["l1t"], *b, stream=sh)
+        q.svdq_linear_w4a4(b[0], b[1], L["qw"], L["sw"], b[2], L["l2t"], L["bias"], out, stream=sh, activation=act)
+
+    def fused(s):
+        run(up, bu, xs[s % R], h, "gelu_tanh")
+        run(dn, bd, h, y)
+
+    def separate(s):
+        run(up, bu, xs[s % R], h)
+        run(dn, bd, torch.nn.functional.gelu(h, approximate="tanh"), y)
+
+    def up_plain(s):
+        run(up, bu, xs[s % R], h)
+
+    def up_gelu(s):
+        run(up, bu, xs[s % R], h, "gelu_tanh")
+
+    def gelu_pass(s):
+        torch.nn.functional.gelu(h, approximate="tanh")
+
+    def timed(fn, n):
+        for s in range(min(n, 10)):
+            fn(s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for s in range(n):
+            fn(s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    n = max(1, args.steps)
+    res = {}
+    for name, fn in (("pair_gelu_fused_us", fused), ("pair_gelu_separate_us", separate),
+                     ("up_plain_us", up_plain), ("up_gelu_fused_us", up_gelu), ("gelu_pass_torch_us", gelu_pass)):
+        log(f"[mlp pair] {name}")
+        res[name] = round(timed(fn, n), 2)
+    ops = 2.0 * M * F * D * 2 + 2.0 * M * cu.rank * (D + F) + 2.0 * M * cd.rank * (F + D)
+    out = {
+        "metric": f"FLUX MLP pair (up {D}->{F} + GELU, down {F}->{D}, M{M}, r{cu.rank}) step time",
+        "unit": "us",
+        "steps": n,
+        "config": {"workload": f"svdq_w4a4 up M{M} K{D} N{F} r{cu.rank} + gelu_tanh + down M{M} K{F} N{D} r{cd.rank}",
+                   "rotating_buffer_sets": R},
+        **res,
+        "pair_TOPS_fused": round(ops / (res["pair_gelu_fused_us"] * 1e-6) / 1e12, 1),
+        "gelu_epilogue_cost_us": round(res["up_gelu_fused_us"] - res["up_plain_us"], 2),
+        "saved_by_fusion_us": round(res["pair_gelu_separate_us"] - res["pair_gelu_fused_us"], 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -233,6 +336,9 @@ def main():
 
     if args.naive_vs_fused:
         naive_vs_fused(args)
+        return
+    if args.mlp_pair:
+        mlp_pair(args)
         return
 
     import torch
