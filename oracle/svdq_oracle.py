@@ -37,6 +37,14 @@ scales), the smoothing/SVD preparation in float64.
   path of the Nunchaku engine. The pages give no formula; the reading here is the tanh form of
   GELU used by FLUX-style MLPs, applied to the layer's unrounded output before the bf16 rounding:
   Y = bf16( gelu_tanh(Y_pre) ), gelu_tanh(v) = v/2 (1 + tanh( sqrt(2/pi) (v + 0.044715 v^3) )).
+
+* The same blog's section on structural rewrites: FLUX's attention projects Q, K and V, splits
+  heads, RMS-normalises Q and K per head (norm_q, norm_k) and applies the rotary embedding; the
+  engine fuses the three projections into one to_qkv (Q, K, V concatenated in that order along the
+  output dimension) followed by a fused norm + rotary operator. Readings: head dimension 128, one
+  RMS weight vector per Q and K shared by all heads, eps = 1e-6, the normalisation applied to the
+  projection's bf16 output (what an unfused pipeline reads), the rotary embedding on interleaved
+  pairs (2i, 2i+1) with per-token cos/sin tables, one bf16 rounding at the end; V unchanged.
 """
 from __future__ import annotations
 
@@ -49,7 +57,7 @@ __all__ = [
     "GROUP", "bf16_round", "smoothing_factors", "svdq_decompose", "int4_quantize_rows",
     "quantize_weights_w4a4", "smooth_activations", "quantize_activations", "lowrank_down",
     "group_sums", "dequant_product", "svdq_linear", "svdq_layer", "quantize_weights_w4a16",
-    "awq_linear", "gelu_tanh", "svdq_linear_gelu",
+    "awq_linear", "gelu_tanh", "svdq_linear_gelu", "qkv_norm_rope",
 ]
 
 
@@ -215,6 +223,34 @@ def svdq_linear_gelu(qa, sa, qw, sw, t=None, l2_bf16=None, bias=None):
     y_pre, _ = svdq_linear(qa, sa, qw, sw, t, l2_bf16, bias)
     g = gelu_tanh(y_pre)
     return g, bf16_round(g.astype(np.float32))
+
+
+def qkv_norm_rope(y_bf16, heads, q_w, k_w, cos, sin, head_dim=128, eps=1e-6):
+    """Per-head RMS normalisation and rotary embedding of the Q and K parts of a fused QKV output.
+
+    y_bf16 float32 [M, 3 * heads * head_dim] holding the projection's bf16 values (Q | K | V);
+    q_w, k_w [head_dim]; cos, sin [M, head_dim / 2] (the angle of pair i of token m). For Q and
+    K, per token and head: u = v / sqrt(mean(v^2) + eps) * w, then pair (u[2i], u[2i+1]) ->
+    (u[2i] c - u[2i+1] s, u[2i] s + u[2i+1] c) with c = cos[m, i], s = sin[m, i]; evaluated in
+    float64 and rounded to bf16 once. V is returned unchanged. Returns float32 holding bf16."""
+    y = np.asarray(y_bf16, dtype=np.float64)
+    M, N = y.shape
+    assert N == 3 * heads * head_dim
+    out = y.copy()
+    c = np.asarray(cos, dtype=np.float64)[:, None, :]
+    s = np.asarray(sin, dtype=np.float64)[:, None, :]
+    for part, w in ((0, q_w), (1, k_w)):
+        v = y[:, part * heads * head_dim:(part + 1) * heads * head_dim].reshape(M, heads, head_dim)
+        rms = np.sqrt(np.mean(v * v, axis=2, keepdims=True) + eps)
+        u = v / rms * np.asarray(w, dtype=np.float64)[None, None, :]
+        a, b = u[:, :, 0::2], u[:, :, 1::2]
+        r = np.empty_like(u)
+        r[:, :, 0::2] = a * c - b * s
+        r[:, :, 1::2] = a * s + b * c
+        out[:, part * heads * head_dim:(part + 1) * heads * head_dim] = r.reshape(M, heads * head_dim)
+    res = bf16_round(out.astype(np.float32))
+    res[:, 2 * heads * head_dim:] = np.asarray(y_bf16, dtype=np.float32)[:, 2 * heads * head_dim:]
+    return res
 
 
 def svdq_layer(x, inv, l1_bf16, l2_bf16, resid, bias=None):

@@ -451,3 +451,50 @@ def test_svdq_linear_gelu_is_gelu_of_the_layer():
     assert np.mean(g == gr) > 0.999 and np.all(np.abs(g - gr) <= 2.0 ** -8 * np.abs(gr) + 1e-30)
     # negative pre-activations shrink towards 0, positive ones stay close to themselves
     assert np.all(np.abs(g64) <= np.abs(out["y64"]) + 1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# fused QKV: per-head RMS normalisation and rotary embedding of Q and K
+# ---------------------------------------------------------------------------------------------
+def _qkv_case(M=5, heads=3, seed=81):
+    D = 128
+    rng = np.random.default_rng(seed)
+    y = oracle.bf16_round(rng.standard_normal((M, 3 * heads * D)).astype(np.float32) * 3.0)
+    q_w = rng.uniform(0.5, 1.5, D)
+    k_w = rng.uniform(0.5, 1.5, D)
+    ang = rng.uniform(-np.pi, np.pi, (M, D // 2))
+    return y, heads, q_w, k_w, np.cos(ang), np.sin(ang), ang
+
+
+def test_qkv_norm_against_torch_rms_norm_and_identity_rotation():
+    """With zero angles the Q/K parts are torch's RMS norm (float64), rounded to bf16; V passes."""
+    import torch
+    y, H, q_w, k_w, _, _, _ = _qkv_case()
+    M, D = y.shape[0], 128
+    out = oracle.qkv_norm_rope(y, H, q_w, k_w, np.ones((M, D // 2)), np.zeros((M, D // 2)))
+    for part, w in ((0, q_w), (1, k_w)):
+        v = torch.from_numpy(y[:, part * H * D:(part + 1) * H * D].astype(np.float64).reshape(M, H, D))
+        ref = torch.nn.functional.rms_norm(v, (D,), torch.from_numpy(w), eps=1e-6).numpy().reshape(M, H * D)
+        assert np.array_equal(out[:, part * H * D:(part + 1) * H * D], oracle.bf16_round(ref.astype(np.float32)))
+    assert np.array_equal(out[:, 2 * H * D:], y[:, 2 * H * D:])
+
+
+def test_qkv_rotary_is_a_complex_rotation_of_pairs():
+    """Rotating pair (a, b) by angle t equals (a + ib) e^{it}; pair norms are preserved; rotating
+    by t then by -t restores the normalised values (checked before the bf16 rounding)."""
+    y, H, q_w, k_w, c, s, ang = _qkv_case(seed=82)
+    M, D = y.shape[0], 128
+    ones, zeros = np.ones((M, D // 2)), np.zeros((M, D // 2))
+    plain = oracle.qkv_norm_rope(y, H, q_w, k_w, ones, zeros)
+    rot = oracle.qkv_norm_rope(y, H, q_w, k_w, c, s)
+    # recompute unrounded normalised Q to compare in float64
+    v = y[:, :H * D].astype(np.float64).reshape(M, H, D)
+    u = v / np.sqrt(np.mean(v * v, axis=2, keepdims=True) + 1e-6) * q_w
+    z = (u[:, :, 0::2] + 1j * u[:, :, 1::2]) * np.exp(1j * ang)[:, None, :]
+    ref = np.empty_like(u)
+    ref[:, :, 0::2], ref[:, :, 1::2] = z.real, z.imag
+    assert np.array_equal(rot[:, :H * D], oracle.bf16_round(ref.reshape(M, H * D).astype(np.float32)))
+    # norms of the pairs are preserved up to the bf16 rounding of both sides
+    pn = lambda a: np.hypot(a[:, 0::2], a[:, 1::2])
+    assert np.allclose(pn(rot[:, :2 * H * D]), pn(plain[:, :2 * H * D]), rtol=2 ** -6, atol=1e-6)
+    assert np.array_equal(rot[:, 2 * H * D:], y[:, 2 * H * D:])
