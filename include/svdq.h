@@ -83,6 +83,7 @@ extern "C" {
 #define SVDQ_ABI_VERSION 1
 #define SVDQ_GROUP 64
 #define SVDQ_MAX_RANK 256
+#define SVDQ_QKV_HEAD_DIM 128
 
 enum svdq_status {
   SVDQ_OK = 0,
@@ -167,6 +168,24 @@ int svdq_linear_w4a4(const uint8_t* qact, const float* ascale, const uint8_t* qw
 int svdq_linear_w4a4_gelu(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                           const void* lora_act, const void* l2t, int r, const void* bias, void* y,
                           int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Fused QKV projection (the Diffusers blog on Nunchaku Lite, section on structural rewrites: FLUX's
+ * to_q, to_k, to_v fused into one to_qkv, Q -> K -> V along the output dimension, followed by a
+ * fused per-head norm of Q and K and the rotary embedding). Computes svdq_linear_w4a4's
+ * Y = bf16(...) for N = 3 * heads * 128 and then, for the Q columns [0, 128 heads) and the K
+ * columns [128 heads, 256 heads), per token m and head of 128 values v:
+ *     u = v / sqrt(mean(v^2) + 1e-6) * w            (w = q_norm_w or k_norm_w, float32 [128])
+ *     (u[2i], u[2i+1]) -> (u[2i] c - u[2i+1] s, u[2i] s + u[2i+1] c)
+ *                                                   (c = rope_cos[m*64 + i], s = rope_sin[m*64 + i])
+ * rounded to bf16 once; the V columns are stored as computed. rope_cos / rope_sin float32 [M, 64]
+ * hold the angle of each pair of each token. Readings (the pages give no formulas): RMS norm with
+ * eps 1e-6 applied to the projection's bf16 output, interleaved pairs.
+ * Errors: those of svdq_linear_w4a4; SVDQ_ERR_NULL for a missing or unaligned norm/rotary table;
+ * SVDQ_ERR_SHAPE if heads < 1 or N != 3 * heads * 128. */
+int svdq_linear_w4a4_qkv(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                         const void* lora_act, const void* l2t, int r, const void* bias, void* y,
+                         int64_t M, int64_t N, int64_t K, int heads, const float* q_norm_w, const float* k_norm_w,
+                         const float* rope_cos, const float* rope_sin, void* stream);
 
 /* W4A16 projection (awq_w4a16 layers of the Diffusers blog): Y = bf16( X dequant(qweight, scales) + b ),
  * X bf16 [M, K], packed weights in the W4A16 block layout, scales bf16 [K/64, N], bias bf16 [N] or NULL.

@@ -35,6 +35,8 @@ _SIGNATURES = {
     "svdq_quantize_act": (_int, [_vp, _i64, _i64, _vp, _vp, _int, _vp, _vp, _vp, _vp]),
     "svdq_linear_w4a4": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _vp]),
     "svdq_linear_w4a4_gelu": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "svdq_linear_w4a4_qkv": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _int, _vp, _vp,
+                                    _vp, _vp, _vp]),
     "awq_linear_w4a16": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "svdq_debug_group_sums": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp]),
 }
@@ -209,6 +211,36 @@ def svdq_linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, bias, y=None,
         _dev_ptr(l2t, "l2t", _bf16(), (N, r)) if r else None, r,
         _dev_ptr(bias, "bias", _bf16(), (N,)), _dev_ptr(y, "y", _bf16(), (M, N)), M, N, K, _stream(stream))
     _check(fn, st)
+    return y
+
+
+def svdq_linear_w4a4_qkv(qact, ascale, qweight, wscale, lora_act, l2t, bias, heads, q_norm_w, k_norm_w, rope_cos,
+                         rope_sin, y=None, stream=None):
+    """Kernel (b) for a fused QKV projection (N = 3 * heads * 128) with the per-head RMS norm of Q
+    and K (weights float32 [128]) and the rotary embedding (rope_cos / rope_sin float32 [M, 64])
+    in its epilogue. Returns y bf16 [M, N]."""
+    import torch
+    G, M = ascale.shape
+    K = G * GROUP
+    N = wscale.shape[1]
+    if qact.numel() != M * K // 2:
+        raise ValueError("qact size does not match K*M/2")
+    r = 0 if l2t is None else l2t.shape[1]
+    if qweight.numel() != N * K // 2:
+        raise ValueError("qweight size does not match [N, K/2]")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=qact.device)
+    f32 = (torch.float32,)
+    st = load_library().svdq_linear_w4a4_qkv(
+        _dev_ptr(qact, "qact", (torch.uint8,)), _dev_ptr(ascale, "ascale", f32, (K // GROUP, M)),
+        _dev_ptr(qweight, "qweight", (torch.uint8,)), _dev_ptr(wscale, "wscale", f32, (K // GROUP, N)),
+        _dev_ptr(lora_act, "lora_act", _bf16(), (M, r)) if r else None,
+        _dev_ptr(l2t, "l2t", _bf16(), (N, r)) if r else None, r,
+        _dev_ptr(bias, "bias", _bf16(), (N,)), _dev_ptr(y, "y", _bf16(), (M, N)), M, N, K, int(heads),
+        _dev_ptr(q_norm_w, "q_norm_w", f32, (128,)), _dev_ptr(k_norm_w, "k_norm_w", f32, (128,)),
+        _dev_ptr(rope_cos, "rope_cos", f32, (M, 64)), _dev_ptr(rope_sin, "rope_sin", f32, (M, 64)),
+        _stream(stream))
+    _check("svdq_linear_w4a4_qkv", st)
     return y
 
 

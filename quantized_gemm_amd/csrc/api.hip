@@ -52,7 +52,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_LA
 
 int linear_w4a4(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                 const void* lora_act, const void* l2t, int r, const void* bias, void* y, int64_t M, int64_t N,
-                int64_t K, bool gelu, void* stream) {
+                int64_t K, const svdq::W4A4Epilogue& epi, void* stream) {
   if (qact == nullptr || ascale == nullptr || qweight == nullptr || wscale == nullptr || y == nullptr)
     return SVDQ_ERR_NULL;
   if (!aligned16(qact) || !aligned16(ascale) || !aligned16(qweight) || !aligned16(wscale) || !aligned16(y) ||
@@ -66,7 +66,7 @@ int linear_w4a4(const uint8_t* qact, const float* ascale, const uint8_t* qweight
   return launch_status(svdq::launch_w4a4_gemm(qact, ascale, qweight, wscale, static_cast<const uint16_t*>(lora_act),
                                               static_cast<const uint16_t*>(l2t), r,
                                               static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), (int)M,
-                                              (int)N, (int)K, gelu, static_cast<hipStream_t>(stream)));
+                                              (int)N, (int)K, epi, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -110,13 +110,32 @@ int svdq_quantize_act(const void* x, int64_t M, int64_t K, const float* inv_smoo
 int svdq_linear_w4a4(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                      const void* lora_act, const void* l2t, int r, const void* bias, void* y, int64_t M, int64_t N,
                      int64_t K, void* stream) {
-  return linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, r, bias, y, M, N, K, false, stream);
+  return linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, r, bias, y, M, N, K, svdq::W4A4Epilogue{}, stream);
 }
 
 int svdq_linear_w4a4_gelu(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                           const void* lora_act, const void* l2t, int r, const void* bias, void* y, int64_t M,
                           int64_t N, int64_t K, void* stream) {
-  return linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, r, bias, y, M, N, K, true, stream);
+  svdq::W4A4Epilogue epi;
+  epi.gelu = true;
+  return linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, r, bias, y, M, N, K, epi, stream);
+}
+
+int svdq_linear_w4a4_qkv(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                         const void* lora_act, const void* l2t, int r, const void* bias, void* y, int64_t M,
+                         int64_t N, int64_t K, int heads, const float* q_norm_w, const float* k_norm_w,
+                         const float* rope_cos, const float* rope_sin, void* stream) {
+  if (q_norm_w == nullptr || k_norm_w == nullptr || rope_cos == nullptr || rope_sin == nullptr) return SVDQ_ERR_NULL;
+  if (!aligned16(q_norm_w) || !aligned16(k_norm_w) || !aligned16(rope_cos) || !aligned16(rope_sin))
+    return SVDQ_ERR_NULL;
+  if (heads < 1 || N != int64_t(3) * heads * SVDQ_QKV_HEAD_DIM) return SVDQ_ERR_SHAPE;
+  svdq::W4A4Epilogue epi;
+  epi.qkv_heads = heads;
+  epi.q_norm_w = q_norm_w;
+  epi.k_norm_w = k_norm_w;
+  epi.rope_cos = rope_cos;
+  epi.rope_sin = rope_sin;
+  return linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, r, bias, y, M, N, K, epi, stream);
 }
 
 int awq_linear_w4a16(const void* x, const uint8_t* qweight, const void* scales, const void* bias, void* y, int64_t M,

@@ -73,6 +73,44 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// RMS norm + rotary embedding of one row of a 128-wide head, 8 values per lane, the row spread
+// over 16 consecutive lanes (lane group of tid / 16): v holds the bf16 values of columns
+// c8 .. c8+7; u = v / sqrt(mean(v^2) + 1e-6) * w, then pair (u[2i], u[2i+1]) is rotated by the
+// angle of pair i of token m (cos/sin tables [M, 64]); one bf16 rounding.
+__device__ __forceinline__ uint4 qk_norm_rope(uint4 v, const float* __restrict__ w, const float* __restrict__ rcos,
+                                              const float* __restrict__ rsin, int m, int c8) {
+  const uint32_t pw[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __uint_as_float(pw[e] << 16);
+    f[2 * e + 1] = __uint_as_float(pw[e] & 0xFFFF0000u);
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
+#pragma unroll
+  for (int mask = 1; mask < 16; mask <<= 1) ss += __shfl_xor(ss, mask, kWave);
+  const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + 1e-6f);
+  const float4 w0 = *reinterpret_cast<const float4*>(w + c8);
+  const float4 w1 = *reinterpret_cast<const float4*>(w + c8 + 4);
+  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  const float4 c = *reinterpret_cast<const float4*>(rcos + (size_t)m * 64 + c8 / 2);
+  const float4 s = *reinterpret_cast<const float4*>(rsin + (size_t)m * 64 + c8 / 2);
+  const float cv[4] = {c.x, c.y, c.z, c.w};
+  const float sv[4] = {s.x, s.y, s.z, s.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float a = f[2 * p] * rinv * wv[2 * p];
+    const float b = f[2 * p + 1] * rinv * wv[2 * p + 1];
+    const float ra = __builtin_fmaf(a, cv[p], -b * sv[p]);
+    const float rb = __builtin_fmaf(a, sv[p], b * cv[p]);
+    o[p] = (uint32_t)f32_to_bf16(ra) | ((uint32_t)f32_to_bf16(rb) << 16);
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
+}
+
 __device__ __forceinline__ uint4 unpack_chunk(uint32_t w0, uint32_t w1) {
   int o0, e0, o1, e1;
   unpack_nibbles_x16(w0, o0, e0);
@@ -95,7 +133,9 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qw,
     const float* __restrict__ sw, const uint16_t* __restrict__ tlr, const uint16_t* __restrict__ l2t, int r,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n,
-    int gelu, int32_t* __restrict__ dbg, int dm0, int dn0, int dtm, int dtn) {
+    int gelu, int qkv_heads, const float* __restrict__ q_norm_w, const float* __restrict__ k_norm_w,
+    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int32_t* __restrict__ dbg, int dm0,
+    int dn0, int dtm, int dtn) {
   __shared__ __align__(16) uint8_t lds[kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -345,6 +385,11 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
       }
     }
     __syncthreads();
+    // Fused QKV (the structural-rewrite section of the Diffusers blog on Nunchaku Lite): the tile's
+    // 128 columns are one head (block-uniform part: 0 = Q, 1 = K, 2 = V). Q and K rows are RMS
+    // normalised per head and rotated pairwise; V passes unchanged.
+    const int qkv_part = qkv_heads > 0 ? n0 / (qkv_heads * kBN) : 2;
+    const float* norm_w = qkv_part == 0 ? q_norm_w : k_norm_w;
     // 128 rows x 256 bytes: thread -> (row = 16 * pass + tid / 16, 16-byte chunk tid % 16)
 #pragma unroll
     for (int pass = 0; pass < kBM / 16; ++pass) {
@@ -352,7 +397,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
       const int c8 = (tid & 15) * 8;
       const int m = m0 + row;
       const int n = n0 + c8;
-      const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kEpiPitch + c8);
+      uint4 v = *reinterpret_cast<const uint4*>(tile + row * kEpiPitch + c8);
+      if (qkv_part < 2) v = qk_norm_rope(v, norm_w, rope_cos, rope_sin, min(m, M - 1), c8);
       // Y is written once and not read here: a non-temporal store keeps it from evicting the
       // activation and weight tiles that other blocks on this XCD are still reading from L2.
       if (m < M && n < N)
@@ -363,12 +409,13 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
 
 template <int NR>
 hipError_t launch_nr(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw, const uint16_t* t,
-                     const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y, int M, int N, int K, bool gelu,
-                     hipStream_t stream) {
+                     const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y, int M, int N, int K,
+                     const W4A4Epilogue& epi, hipStream_t stream) {
   const int tiles_m = (M + kBM - 1) / kBM;
   const int tiles_n = (N + kBN - 1) / kBN;
   hipLaunchKernelGGL((w4a4_gemm_kernel<NR, false>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, qa, sa, qw,
-                     sw, t, l2t, r, bias, y, M, N, K, tiles_m, tiles_n, gelu ? 1 : 0, nullptr, 0, 0, 0, 0);
+                     sw, t, l2t, r, bias, y, M, N, K, tiles_m, tiles_n, epi.gelu ? 1 : 0, epi.qkv_heads,
+                     epi.q_norm_w, epi.k_norm_w, epi.rope_cos, epi.rope_sin, nullptr, 0, 0, 0, 0);
   return hipGetLastError();
 }
 
@@ -376,25 +423,25 @@ hipError_t launch_nr(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
 
 hipError_t launch_w4a4_gemm(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                             const uint16_t* t, const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y,
-                            int M, int N, int K, bool gelu, hipStream_t stream) {
+                            int M, int N, int K, const W4A4Epilogue& epi, hipStream_t stream) {
   switch (r / 16) {
-    case 0: return launch_nr<0>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 1: return launch_nr<1>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 2: return launch_nr<2>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 3: return launch_nr<3>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 4: return launch_nr<4>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 5: return launch_nr<5>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 6: return launch_nr<6>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 7: return launch_nr<7>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 8: return launch_nr<8>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 9: return launch_nr<9>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 10: return launch_nr<10>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 11: return launch_nr<11>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 12: return launch_nr<12>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 13: return launch_nr<13>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 14: return launch_nr<14>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 15: return launch_nr<15>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
-    case 16: return launch_nr<16>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, gelu, stream);
+    case 0: return launch_nr<0>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 1: return launch_nr<1>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 2: return launch_nr<2>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 3: return launch_nr<3>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 4: return launch_nr<4>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 5: return launch_nr<5>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 6: return launch_nr<6>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 7: return launch_nr<7>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 8: return launch_nr<8>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 9: return launch_nr<9>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 10: return launch_nr<10>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 11: return launch_nr<11>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 12: return launch_nr<12>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 13: return launch_nr<13>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 14: return launch_nr<14>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 15: return launch_nr<15>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+    case 16: return launch_nr<16>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -405,7 +452,8 @@ hipError_t launch_w4a4_group_sums(const uint8_t* qact, const uint8_t* qweight, i
   const int tn0 = n0 / kBN, tn1 = (n0 + tn - 1) / kBN;
   const dim3 grid(tn1 - tn0 + 1, tm1 - tm0 + 1);
   hipLaunchKernelGGL((w4a4_gemm_kernel<0, true>), grid, dim3(kThreads), 0, stream, qact, nullptr, qweight, nullptr,
-                     nullptr, nullptr, 0, nullptr, nullptr, M, N, K, 0, 0, 0, out, m0, n0, tm, tn);
+                     nullptr, nullptr, 0, nullptr, nullptr, M, N, K, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, out, m0,
+                     n0, tm, tn);
   return hipGetLastError();
 }
 

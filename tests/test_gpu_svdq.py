@@ -322,6 +322,68 @@ def test_mlp_pair_chained_on_real_intermediates(gpu):
 
 
 # ---------------------------------------------------------------------------------------------
+# fused QKV: per-head RMS norm + rotary embedding of Q and K in the epilogue
+# ---------------------------------------------------------------------------------------------
+def _qkv_tables(M, heads, seed):
+    rng = np.random.default_rng(seed)
+    q_w = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    k_w = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    pos = np.arange(M, dtype=np.float64)[:, None]
+    freq = 10000.0 ** (-np.arange(64, dtype=np.float64) / 64.0)[None, :]
+    ang = pos * freq + rng.uniform(-0.1, 0.1, (M, 64))
+    return q_w, k_w, np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _run_qkv(gpu, layer, x_bits, heads, tables):
+    import torch
+    import quantized_gemm_amd as q
+    q_w, k_w, cs, sn = tables
+    x = to_dev_bf16(x_bits, gpu)
+    qact, ascale, t = q.svdq_quantize_act(x, layer.inv, layer.l1t)
+    y = q.svdq_linear_w4a4_qkv(qact, ascale, layer.qw, layer.sw, t, layer.l2t, layer.bias, heads,
+                               to_dev(q_w, gpu), to_dev(k_w, gpu), to_dev(cs, gpu), to_dev(sn, gpu))
+    y_plain = q.svdq_linear_w4a4(qact, ascale, layer.qw, layer.sw, t, layer.l2t, layer.bias)
+    torch.cuda.synchronize()
+    return bf16_to_np(y), bf16_to_np(y_plain)
+
+
+def _check_qkv_epilogue(y, y_plain, heads, tables):
+    """The epilogue against the oracle applied to the kernel's own plain output: within one bf16
+    ulp everywhere (float32 on the GPU, float64 in the oracle, one bf16 rounding each), V identical."""
+    q_w, k_w, cs, sn = tables
+    ref = oracle.qkv_norm_rope(y_plain, heads, q_w, k_w, cs, sn)
+    ok = within_one_bf16_ulp(y, ref, abs_floor=2.0 ** -16 * float(np.abs(ref).max()))
+    assert ok.all(), f"QKV epilogue beyond one bf16 ulp at {np.argwhere(~ok)[:5]}"
+    say(f"  Q/K exact fraction {np.mean(y[:, :2 * heads * 128] == ref[:, :2 * heads * 128]):.6f}")
+    assert np.array_equal(y[:, 2 * heads * 128:], y_plain[:, 2 * heads * 128:])
+
+
+def test_qkv_norm_rope_small_ragged(gpu):
+    M, K, heads, r = 200, 256, 2, 16
+    say(f"[qkv] M={M} K={K} heads={heads} r={r}")
+    p = random_w4a4_problem(M, K, 3 * heads * 128, r, seed=91)
+    tables = _qkv_tables(M, heads, seed=92)
+    y, y_plain = _run_qkv(gpu, Layer(p, gpu), p["x_bits"], heads, tables)
+    _check_qkv_epilogue(y, y_plain, heads, tables)
+    # and the whole chain against the oracle's
+    ref = oracle.qkv_norm_rope(p["y"], heads, *tables)
+    mx, mean = tolerance_report(y, ref)
+    say(f"  QKV max|err|/max|ref| = {mx:.3e}, mean rel = {mean:.3e}")
+    assert mx <= MAX_REL and mean <= MEAN_REL
+
+
+@pytest.mark.timeout(600)
+def test_qkv_norm_rope_flux_shape(gpu):
+    """FLUX attention: M 4608, K 3072, 24 heads of 128 (N 9216), rank 32."""
+    p = w4a4_problem("qkv_r32")
+    heads = p["cfg"].N // (3 * 128)
+    say(f"[qkv] FLUX shape, heads={heads}")
+    tables = _qkv_tables(p["cfg"].M, heads, seed=93)
+    y, y_plain = _run_qkv(gpu, Layer(p, gpu), p["x_bits"], heads, tables)
+    _check_qkv_epilogue(y, y_plain, heads, tables)
+
+
+# ---------------------------------------------------------------------------------------------
 # W4A16 projection
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("M,with_bias", [(16, False), (16, True), (1, False), (5, True), (33, False)])

@@ -190,6 +190,11 @@ def test_device_entry_validation(lib):
     assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, None, P, 16, 1 << 27, 64, None) == -2
     assert lib.svdq_linear_w4a4(P, P, P, P, P, None, 32, None, P, 16, 16, 64, None) == -3
     assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, ODD, P, 16, 16, 64, None) == -1
+    # the fused-QKV form: norm / rotary tables required, N = 3 * heads * 128
+    assert lib.svdq_linear_w4a4_qkv(P, P, P, P, None, None, 0, None, P, 16, 384, 64, 1, None, P, P, P, None) == -1
+    assert lib.svdq_linear_w4a4_qkv(P, P, P, P, None, None, 0, None, P, 16, 384, 64, 1, P, P, P, ODD, None) == -1
+    assert lib.svdq_linear_w4a4_qkv(P, P, P, P, None, None, 0, None, P, 16, 384, 64, 2, P, P, P, P, None) == -2
+    assert lib.svdq_linear_w4a4_qkv(P, P, P, P, None, None, 0, None, P, 16, 384, 64, 0, P, P, P, P, None) == -2
     # the GELU form validates exactly like the plain one
     assert lib.svdq_linear_w4a4_gelu(P, P, P, P, None, None, 0, None, None, 16, 16, 64, None) == -1
     assert lib.svdq_linear_w4a4_gelu(P, P, P, P, None, None, 0, None, P, 16, 24, 64, None) == -2
@@ -211,4 +216,5 @@ def test_valid_arguments_without_gpu_report_arch(lib):
     assert lib.svdq_quantize_act(P, 16, 64, None, None, 0, P, P, None, None) == -5
     assert lib.svdq_linear_w4a4(P, P, P, P, None, None, 0, None, P, 16, 16, 64, None) == -5
     assert lib.svdq_linear_w4a4_gelu(P, P, P, P, None, None, 0, None, P, 16, 16, 64, None) == -5
+    assert lib.svdq_linear_w4a4_qkv(P, P, P, P, None, None, 0, None, P, 16, 384, 64, 1, P, P, P, P, None) == -5
     assert lib.awq_linear_w4a16(P, P, P, None, P, 16, 16, 64, None) == -5
