@@ -26,6 +26,10 @@ with the three step times.
 3072 -> 12288, r32) with the tanh-form GELU fused into its epilogue, then the down projection
 (12288 -> 3072, r32) quantizing that output. It compares the same chain with the GELU run as a
 separate bf16 pass (torch) between the two layers, and prints one JSON line.
+
+``--qkv-epilogue`` times the fused QKV projection of FLUX attention (M4608, 3072 -> 3 x 24 heads x
+128, r32) with the per-head RMS norm of Q and K and the rotary embedding in the GEMM epilogue,
+against the plain projection followed by the same norm + rotation in torch (bf16 in and out).
 """
 from __future__ import annotations
 
@@ -62,6 +66,8 @@ def parse():
                     help="time the 4-bit branch alone, the naive unfused low-rank branch and the fused kernels")
     ap.add_argument("--mlp-pair", action="store_true",
                     help="time the up (+GELU) -> down MLP pair, GELU fused vs a separate GELU pass")
+    ap.add_argument("--qkv-epilogue", action="store_true",
+                    help="time the fused QKV projection with the Q/K norm + rotary epilogue vs torch after it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this size (a known-traffic "
                          "kernel that scales the HBM byte counters)")
@@ -327,6 +333,114 @@ def mlp_pair(args):
     print(json.dumps(out), flush=True)
 
 
+def qkv_epilogue(args):
+    import torch
+    import synth
+    import quantized_gemm_amd as q
+    from quantized_gemm_amd import prep
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    q.load_library()
+    q.svdq_check_device()
+    cfg = synth.CONFIGS["qkv_r32"]
+    M, K, N, r = cfg.M, cfg.K, cfg.N, cfg.rank
+    heads, D = N // (3 * 128), 128
+    log(f"[qkv] preparing M={M} K={K} N={N} ({heads} heads) r={r}")
+    inp = synth.make_layer_inputs(cfg)
+    d = prep.decompose(synth.f32_from_bf16_bits(inp["x"]), synth.f32_from_bf16_bits(inp["w"]), r)
+    qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, d["resid"])
+    l1t, l2t = q.svdq_pack_lowrank(d["l1"], d["l2"])
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x = bf16_dev(inp["x"])
+    inv = torch.from_numpy(d["inv_smooth"]).to(dev)
+    qw_d, sw_d, l1t_d, l2t_d = torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev), bf16_dev(l1t), bf16_dev(l2t)
+    bias = bf16_dev(inp["bias"])
+    rng = np.random.default_rng(5)
+    q_w = torch.from_numpy(rng.uniform(0.5, 1.5, D).astype(np.float32)).to(dev)
+    k_w = torch.from_numpy(rng.uniform(0.5, 1.5, D).astype(np.float32)).to(dev)
+    ang = np.arange(M)[:, None] * 10000.0 ** (-np.arange(64) / 64.0)[None, :]
+    cs = torch.from_numpy(np.cos(ang).astype(np.float32)).to(dev)
+    sn = torch.from_numpy(np.sin(ang).astype(np.float32)).to(dev)
+    qact, asc, t = q.svdq_quantize_act(x, inv, l1t_d)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def plain(s):
+        q.svdq_linear_w4a4(qact, asc, qw_d, sw_d, t, l2t_d, bias, y, stream=sh)
+
+    def fused(s):
+        q.svdq_linear_w4a4_qkv(qact, asc, qw_d, sw_d, t, l2t_d, bias, heads, q_w, k_w, cs, sn, y, stream=sh)
+
+    def torch_norm_rope(s):
+        # what the unfused FLUX attention runs after the projection (float32 math, bf16 out)
+        qk = y[:, :2 * heads * D].view(M, 2, heads, D).float()
+        w = torch.stack([q_w, k_w])[None, :, None, :]
+        u = qk * torch.rsqrt(qk.pow(2).mean(-1, keepdim=True) + 1e-6) * w
+        a, b = u[..., 0::2], u[..., 1::2]
+        c, s_ = cs[:, None, None, :], sn[:, None, None, :]
+        out = torch.stack([a * c - b * s_, a * s_ + b * c], dim=-1).flatten(-2)
+        return out.to(torch.bfloat16)
+
+    def separate(s):
+        plain(s)
+        torch_norm_rope(s)
+
+    def timed(fn, n):
+        for s in range(min(n, 10)):
+            fn(s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for s in range(n):
+            fn(s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    def paired(fa, fb, n):
+        """A/B: the two launches alternate in one loop, each between its own pair of events, so
+        both see the same clock and cache state (every event adds the same small cost to both)."""
+        for s in range(10):
+            fa(s)
+            fb(s)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for s in range(n):
+            evs[s][0].record(stream)
+            fa(s)
+            evs[s][1].record(stream)
+            fb(s)
+            evs[s][2].record(stream)
+        torch.cuda.synchronize()
+        ta = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+        tb = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+        return ta, tb
+
+    n = max(1, args.steps)
+    res = {}
+    log("[qkv] plain / fused, interleaved")
+    tp, tf = paired(plain, fused, n)
+    res["plain_us"], res["fused_norm_rope_us"] = round(tp, 2), round(tf, 2)
+    for name, fn in (("plain_then_torch_us", separate), ("torch_norm_rope_us", torch_norm_rope)):
+        log(f"[qkv] {name}")
+        res[name] = round(timed(fn, n), 2)
+    out = {
+        "metric": f"fused QKV projection with the Q/K RMS norm + rotary epilogue (M{M} K{K} N{N}, {heads} heads, r{r})",
+        "unit": "us",
+        "steps": n,
+        "config": {"workload": f"svdq_w4a4 qkv_r32 M{M} K{K} N{N} r{r} + qk norm + rope"},
+        **res,
+        "epilogue_cost_us": round(res["fused_norm_rope_us"] - res["plain_us"], 2),
+        "saved_by_fusion_us": round(res["plain_then_torch_us"] - res["fused_norm_rope_us"], 2),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -339,6 +453,9 @@ def main():
         return
     if args.mlp_pair:
         mlp_pair(args)
+        return
+    if args.qkv_epilogue:
+        qkv_epilogue(args)
         return
 
     import torch
