@@ -78,9 +78,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# sources whose kernels a launch of the named unit runs (the W4A4 kernel body lives in a header)
+KERNEL_SOURCES = {"w4a4_gemm.hip": ["w4a4_gemm_kernel.h", "w4a4_gemm.hip"]}
+
+
 def kernel_source_hash(name: str) -> str:
-    with open(os.path.join(ROOT, "quantized_gemm_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for part in KERNEL_SOURCES.get(name, [name]):
+        with open(os.path.join(ROOT, "quantized_gemm_amd", "csrc", part), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel_file: str, workload: str):

@@ -24,7 +24,8 @@ LIB = os.path.join(LIBDIR, "libsvdq.so")
 # per-kernel register / scratch / occupancy figures reported by the compiler during the build
 RESOURCES = os.path.join(LIBDIR, "kernel_resources.txt")
 
-SOURCES = ["api.hip", "quant_act.hip", "w4a4_gemm.hip", "w4a16_gemv.hip", "pack.cpp"]
+SOURCES = ["api.hip", "quant_act.hip", "w4a4_gemm.hip", "w4a4_gemm_gelu.hip", "w4a4_gemm_qkv.hip", "w4a16_gemv.hip",
+           "pack.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math",

@@ -26,6 +26,14 @@ hipError_t launch_w4a4_gemm(const uint8_t* qact, const float* ascale, const uint
                             const uint16_t* t, const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y,
                             int M, int N, int K, const W4A4Epilogue& epi, hipStream_t stream);
 
+// The GELU and fused-QKV variants (their own translation units).
+hipError_t launch_w4a4_gemm_gelu(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                                 const uint16_t* t, const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y,
+                                 int M, int N, int K, const W4A4Epilogue& epi, hipStream_t stream);
+hipError_t launch_w4a4_gemm_qkv(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                                const uint16_t* t, const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y,
+                                int M, int N, int K, const W4A4Epilogue& epi, hipStream_t stream);
+
 hipError_t launch_w4a4_group_sums(const uint8_t* qact, const uint8_t* qweight, int M, int N, int K, int m0, int n0,
                                   int tm, int tn, int32_t* out, hipStream_t stream);
 

@@ -1,449 +1,17 @@
-// Kernel (b): fused 4-bit product + low-rank up projection of the SVDQuant linear on gfx950.
-//
-// Engine-design figure of the Nunchaku README, panel (b): the up projection T L2 and the 4-bit
-// product write the same output, so both accumulate into one float32 tile and Y is stored once.
-//
-// CDNA4 has no INT4 MFMA. Packed nibbles are widened to int8 holding 16 * code (two bit
-// operations per 8 codes) and fed to v_mfma_i32_32x32x32_i8; two chained instructions cover one
-// quantization group of 64, so they yield 256 * P[g] for a 32x32 tile, P being the exact integer
-// group sum. The MFMA's C operand is the constant 0x4B400000 (the float 1.5 * 2^23): the integer
-// result is then the bit pattern of the float 1.5*2^23 + 256 P (exact, |256 P| <= 2^20), so no
-// int-to-float conversion is needed. The group-boundary rescale is two FMAs per element:
-//     u = D * sw[g, n] - (1.5 * 2^23) * sw[g, n];     acc += u * sa[g, m]
-// and the common factor 1/256 is applied once at the end. The epilogue adds T L2 with bf16
-// MFMAs accumulating straight into the same float32 tile (C operand = acc), adds the bias and
-// stores bf16.
-//
-// Tiling: block = 128 x 128 outputs, 4 waves stacked along M; wave tile 32 tokens x 128 columns
-// = 1 x 4 MFMA tiles of 32 x 32; two blocks per CU. One K step is one group of 64.
-//   * Activations: each wave owns its 32 tokens, so it loads their packed codes straight from
-//     global memory (group-major layout: 1 KiB contiguous per wave and group, one 16-byte load per
-//     lane), two groups ahead, and widens them in registers.
-//   * Residual weights are shared by the 4 waves: the block loads the group's 128 columns (4 KiB,
-//     one 16-byte load per thread, two groups ahead), widens them once into LDS as int8 (rows
-//     padded to 80 bytes: conflict-free 16-byte operand reads) beside the group's 128 + 128 scales.
-//     Three LDS stages, one barrier per group.
-//   * Within a wave the rescale of group g-1 is interleaved with the MFMAs of group g: the FMAs
-//     never wait for a fresh MFMA result and the matrix core runs under the VALU work.
-// Tile order: consecutive block ids land on different XCDs (round-robin dispatch), so block id b
-// is mapped to a contiguous range of tiles per XCD, and tiles are walked in groups of 8 tile rows
-// so that the blocks resident on one XCD share their activation and weight tiles in its L2.
-#include <type_traits>
-
-#include "svdq_device.h"
-#include "svdq_launch.h"
+// Kernel (b): the plain W4A4 layer (no activation) and the exact group-sum export, and the
+// dispatch of svdq_linear_w4a4* to the translation unit that holds each epilogue's kernels (each
+// unit instantiates the kernel for the 17 ranks; splitting them lets the build compile in parallel).
+#include "w4a4_gemm_kernel.h"
 
 namespace svdq {
-
-namespace {
-
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kThreads = 256;
-constexpr int kPitch = 80;  // bytes per widened LDS weight row: 64 int8 codes + 16 bytes of padding
-constexpr int kScaleOff = kBN * kPitch;                    // sa[128] then sw[128]
-constexpr int kStageBytes = kScaleOff + (kBM + kBN) * 4;
-constexpr int kEpiPitch = kBN + 8;                         // bf16 per row of the output staging tile
-constexpr int kStages = 3;
-constexpr int kLdsBytes = (kStages * kStageBytes > kBM * kEpiPitch * 2) ? kStages * kStageBytes : kBM * kEpiPitch * 2;
-constexpr int kNumXcd = 8;
-constexpr int kGroupRows = 8;
-
-__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int T = tiles_m * tiles_n;
-  const int xcd = bid % kNumXcd, slot = bid / kNumXcd;
-  const int per = T / kNumXcd, rem = T % kNumXcd;
-  const int t = xcd * per + min(xcd, rem) + slot;
-  const int width = kGroupRows * tiles_n;
-  const int first_m = (t / width) * kGroupRows;
-  const int gsz = min(tiles_m - first_m, kGroupRows);
-  tm = first_m + (t % width) % gsz;
-  tn = (t % width) / gsz;
-}
-
-// GELU in its tanh form (the GELU/MLP path named in the Diffusers blog on Nunchaku Lite), through
-// the logistic identity (1 + tanh(u)) / 2 = 1 / (1 + e^(-2u)):
-//     gelu(x) = x / (1 + 2^(-2 log2(e) u)),   u = sqrt(2/pi) (x + 0.044715 x^3),
-// with the hardware exp2 and reciprocal (each within about an ulp; no cancellation for negative
-// x, and the limits come out exactly: x -> -inf gives -0, x -> +inf gives x).
-__device__ __forceinline__ float gelu_tanh(float x) {
-  constexpr float kC = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
-  const float u = x * __builtin_fmaf(0.044715f, x * x, 1.0f);
-  const float e = __builtin_amdgcn_exp2f(kC * u);
-  return x * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-// RMS norm + rotary embedding of one row of a 128-wide head, 8 values per lane, the row spread
-// over 16 consecutive lanes (lane group of tid / 16): v holds the bf16 values of columns
-// c8 .. c8+7; u = v / sqrt(mean(v^2) + 1e-6) * w, then pair (u[2i], u[2i+1]) is rotated by the
-// angle of pair i of token m (cos/sin tables [M, 64]); one bf16 rounding.
-__device__ __forceinline__ uint4 qk_norm_rope(uint4 v, const float* __restrict__ w, const float* __restrict__ rcos,
-                                              const float* __restrict__ rsin, int m, int c8) {
-  const uint32_t pw[4] = {v.x, v.y, v.z, v.w};
-  float f[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[2 * e] = __uint_as_float(pw[e] << 16);
-    f[2 * e + 1] = __uint_as_float(pw[e] & 0xFFFF0000u);
-  }
-  float ss = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
-#pragma unroll
-  for (int mask = 1; mask < 16; mask <<= 1) ss += __shfl_xor(ss, mask, kWave);
-  const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + 1e-6f);
-  const float4 w0 = *reinterpret_cast<const float4*>(w + c8);
-  const float4 w1 = *reinterpret_cast<const float4*>(w + c8 + 4);
-  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-  const float4 c = *reinterpret_cast<const float4*>(rcos + (size_t)m * 64 + c8 / 2);
-  const float4 s = *reinterpret_cast<const float4*>(rsin + (size_t)m * 64 + c8 / 2);
-  const float cv[4] = {c.x, c.y, c.z, c.w};
-  const float sv[4] = {s.x, s.y, s.z, s.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float a = f[2 * p] * rinv * wv[2 * p];
-    const float b = f[2 * p + 1] * rinv * wv[2 * p + 1];
-    const float ra = __builtin_fmaf(a, cv[p], -b * sv[p]);
-    const float rb = __builtin_fmaf(a, sv[p], b * cv[p]);
-    o[p] = (uint32_t)f32_to_bf16(ra) | ((uint32_t)f32_to_bf16(rb) << 16);
-  }
-  return uint4{o[0], o[1], o[2], o[3]};
-}
-
-__device__ __forceinline__ uint4 unpack_chunk(uint32_t w0, uint32_t w1) {
-  int o0, e0, o1, e1;
-  unpack_nibbles_x16(w0, o0, e0);
-  unpack_nibbles_x16(w1, o1, e1);
-  return uint4{(uint32_t)o0, (uint32_t)e0, (uint32_t)o1, (uint32_t)e1};
-}
-
-template <typename T>
-__device__ __forceinline__ v4i as_v4i(T u) { return __builtin_bit_cast(v4i, u); }
-
-// Raw buffer resource over `bytes` bytes at `base` (offsets past the end read zero). Row counts
-// below 2^27 keep every per-group range and lane offset within 32 bits.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// DEBUG replaces the rescale and the epilogue by a dump of the exact group sums of a window.
-template <int NR, bool DEBUG>
-__global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
-    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qw,
-    const float* __restrict__ sw, const uint16_t* __restrict__ tlr, const uint16_t* __restrict__ l2t, int r,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n,
-    int gelu, int qkv_heads, const float* __restrict__ q_norm_w, const float* __restrict__ k_norm_w,
-    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int32_t* __restrict__ dbg, int dm0,
-    int dn0, int dtm, int dtn) {
-  __shared__ __align__(16) uint8_t lds[kLdsBytes];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  int tm, tn;
-  if constexpr (DEBUG) {
-    tm = blockIdx.y + dm0 / kBM;
-    tn = blockIdx.x + dn0 / kBN;
-  } else {
-    map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  }
-  const int m0 = tm * kBM;
-  const int n0 = tn * kBN;
-  const int G = K / kGroup;
-
-  // Lane l = 32 h + r of the 32x32x32 MFMA: row (A) / column (B) r, and for MFMA s = 0, 1 the 16
-  // codes of 16-code chunk 2h + s of the group (the same chunk for A and B: the k pairing matches).
-  const int r32 = lane & 31;
-  const int h = lane >> 5;
-  const int wrow = 32 * wave;                                  // the wave's first token in the tile
-
-  // Activation loads: lane reads packed bytes [16h, 16h+16) (chunks 2h, 2h+1) of its token's group.
-  // Tokens past M read the last valid token: their outputs are never stored.
-  const uint32_t a_off = (uint32_t)min(m0 + wrow + r32, M - 1) * 32u + 16u * h;
-  // Loader role (block-wide): 16 packed bytes of weight row lrow, and one scale.
-  const int lrow = tid >> 1;
-  const int lhalf = tid & 1;
-  const uint32_t b_off = (uint32_t)min(n0 + lrow, N - 1) * 32u + 16u * lhalf;
-  const bool s_is_a = tid < kBM;
-  const uint32_t s_off = s_is_a ? (uint32_t)min(m0 + tid, M - 1) : (uint32_t)min(n0 + tid - kBM, N - 1);
-  const uint32_t st_b = lrow * kPitch + 32 * lhalf;
-  // Scale slot in the stage: sa of token tid, or sw of column 32 t + c stored at 4 c + t, so that
-  // a lane reads the weight scales of its column in all four column tiles with one 16-byte read.
-  const uint32_t st_s = s_is_a ? (uint32_t)tid : (uint32_t)(kBM + ((tid - kBM) & 31) * 4 + ((tid - kBM) >> 5));
-  // Operand / scale read offsets within a stage.
-  const uint32_t rd_b = r32 * kPitch + 32 * h;
-  const uint32_t rd_sa = kScaleOff + 4 * (wrow + 4 * h);
-  const uint32_t rd_sw = kScaleOff + 4 * (kBM + 4 * r32);
-
-
-  uint4 apk[2], bpk[2];
-  float spk[2];
-  // Buffer loads: the resource holds this group's (wave-uniform) base and size in scalar registers,
-  // the lane supplies its 32-bit byte offset, so no vector instruction computes an address. The
-  // scale array is chosen per wave (threads < kBM are waves 0 and 1).
-  const bool s_is_a_w = __builtin_amdgcn_readfirstlane(tid >> 6) < kBM / kWave;
-  auto gload_a = [&](int slot, int g) {
-    apk[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              buffer_rsrc(qa + (size_t)g * M * 32, (uint32_t)M * 32u), (int)a_off, 0, 0));
-  };
-  auto gload_b = [&](int slot, int g) {
-    bpk[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              buffer_rsrc(qw + (size_t)g * N * 32, (uint32_t)N * 32u), (int)b_off, 0, 0));
-    if constexpr (!DEBUG) {
-      const float* base = s_is_a_w ? sa + (size_t)g * M : sw + (size_t)g * N;
-      const uint32_t bytes = s_is_a_w ? (uint32_t)M * 4u : (uint32_t)N * 4u;
-      spk[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(base, bytes),
-                                                                                   (int)(4u * s_off), 0, 0));
-    }
-  };
-  auto lstore = [&](int slot, uint8_t* st) {
-    *reinterpret_cast<uint4*>(st + st_b) = unpack_chunk(bpk[slot].x, bpk[slot].y);
-    *reinterpret_cast<uint4*>(st + st_b + 16) = unpack_chunk(bpk[slot].z, bpk[slot].w);
-    if constexpr (!DEBUG) {
-      reinterpret_cast<float*>(st + kScaleOff)[st_s] = spk[slot];
-    }
-  };
-
-  v16f acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
-  v16i magic;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) magic[v] = (int)kMagicBits;
-  v16i D[4];     // MFMA results of the previous group, one per column tile
-  float sap[16];  // its activation scales: rows 8q + 4h + s (q, s = 0..3) of the wave's 32 tokens
-  float swp[4];   // its weight scales, one per column tile
-
-  // Rescale of group gp's tile t into the accumulator; for DEBUG the exact group sums are dumped.
-  auto finish_tile = [&](int gp, int t) {
-    if constexpr (DEBUG) {
-      const int n = n0 + 32 * t + r32;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wrow + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (m >= dm0 && m < dm0 + dtm && n >= dn0 && n < dn0 + dtn)
-          dbg[((size_t)gp * dtm + (m - dm0)) * dtn + (n - dn0)] = (D[t][v] - (int)kMagicBits) >> 8;
-      }
-    } else {
-      const float swc = -kMagic * swp[t];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float u = __builtin_fmaf(__int_as_float(D[t][v]), swp[t], swc);
-        acc[t][v] = __builtin_fmaf(u, sap[v], acc[t][v]);
-      }
-    }
-  };
-  // Scales of the group held in stage `sp`, for the next step's rescale.
-  auto read_scales = [&](const uint8_t* sp) {
-    if constexpr (!DEBUG) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f = *reinterpret_cast<const float4*>(sp + rd_sa + 4 * 8 * q);
-        sap[4 * q + 0] = f.x;
-        sap[4 * q + 1] = f.y;
-        sap[4 * q + 2] = f.z;
-        sap[4 * q + 3] = f.w;
-      }
-      {
-        const float4 f = *reinterpret_cast<const float4*>(sp + rd_sw);
-        swp[0] = f.x;
-        swp[1] = f.y;
-        swp[2] = f.z;
-        swp[3] = f.w;
-      }
-    }
-  };
-
-  // One K step g (C = g % 3 is the stage of group g, S = (g+1) % 3 the stage being filled,
-  // P = g & 1 the register slot): widen the wave's activation codes of group g; for each column
-  // tile, read group g's weight operands from stage C, finish the previous group's tile and issue
-  // the tile's MFMAs; store group g+1 into stage S and issue the global loads two groups ahead;
-  // finally read group g's scales (stage C) for the next step, so that their latency hides behind
-  // the barrier. Three stages make one barrier per step sufficient: the stage written in step g
-  // was last read in step g-1.
-  auto step = [&](auto cst, auto sst, auto par, int g, auto first_tag) {
-    constexpr int C = decltype(cst)::value;
-    constexpr int S = decltype(sst)::value;
-    constexpr int P = decltype(par)::value;
-    constexpr bool first = decltype(first_tag)::value;
-    const uint8_t* st = lds + C * kStageBytes;
-    const v4i A0 = as_v4i(unpack_chunk(apk[P].x, apk[P].y));
-    const v4i A1 = as_v4i(unpack_chunk(apk[P].z, apk[P].w));
-    gload_a(P, min(g + 2, G - 1));
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const v4i B0 = *reinterpret_cast<const v4i*>(st + rd_b + 32 * t * kPitch);
-      const v4i B1 = *reinterpret_cast<const v4i*>(st + rd_b + 32 * t * kPitch + 16);
-      if (!first) finish_tile(g - 1, t);
-      D[t] = mfma_i8_32x32x32(A1, B1, mfma_i8_32x32x32(A0, B0, magic));
-    }
-    lstore(P ^ 1, lds + S * kStageBytes);
-    gload_b(P ^ 1, min(g + 3, G - 1));
-    read_scales(st);
-    if constexpr (!DEBUG) {
-      // Issue order: B of tile 0; A widening and its load; then per tile its rescale, the next
-      // tile's B reads and the MFMAs; between tiles 1 and 2 the next stage's widening, LDS stores
-      // and loads.
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read: B tile 0
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU: widen A
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load: A
-      constexpr int kRescale = first ? 0 : 33;
-      // tile 0
-      __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);  // VALU: rescale
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // LDS read: B tile 1
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);         // MFMA
-      // tile 1
-      __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);        // VALU: widen the next B tile
-      __builtin_amdgcn_sched_group_barrier(0x200, 3, 0);         // LDS write
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);         // global load: B, scale
-      // tile 2
-      __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      // tile 3
-      __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      // (the scale reads are left to the scheduler: pinning them to the end raised the register
-      // pressure past 256 VGPRs and spilled)
-    }
-    __syncthreads();
-  };
-
-  gload_a(0, 0);
-  gload_a(1, min(1, G - 1));
-  gload_b(0, 0);
-  gload_b(1, min(1, G - 1));
-  lstore(0, lds);
-  gload_b(0, min(2, G - 1));
-  __syncthreads();
-
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  // Group g uses stage g % 3 and register slot g % 2: the pattern repeats every 6 groups.
-  step(I0(), I1(), I0(), 0, std::true_type());
-  int g = 1;
-  for (; g + 5 < G; g += 6) {
-    step(I1(), I2(), I1(), g, std::false_type());
-    step(I2(), I0(), I0(), g + 1, std::false_type());
-    step(I0(), I1(), I1(), g + 2, std::false_type());
-    step(I1(), I2(), I0(), g + 3, std::false_type());
-    step(I2(), I0(), I1(), g + 4, std::false_type());
-    step(I0(), I1(), I0(), g + 5, std::false_type());
-  }
-  if (g < G) { step(I1(), I2(), I1(), g, std::false_type()); ++g; }
-  if (g < G) { step(I2(), I0(), I0(), g, std::false_type()); ++g; }
-  if (g < G) { step(I0(), I1(), I1(), g, std::false_type()); ++g; }
-  if (g < G) { step(I1(), I2(), I0(), g, std::false_type()); ++g; }
-  if (g < G) { step(I2(), I0(), I1(), g, std::false_type()); ++g; }
-#pragma unroll
-  for (int t = 0; t < 4; ++t) finish_tile(G - 1, t);
-
-  if constexpr (!DEBUG) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[t][v] = acc[t][v] * (1.0f / 256.0f);
-
-    if constexpr (NR > 0) {
-      // T L2 with K = r in steps of 16 on 32x32x16 bf16 MFMAs; lane (r32, h) supplies rank
-      // indices 16q + 8h .. +7 of token / column r32, accumulating into the same float32 tile.
-      const int mt = min(m0 + wrow + r32, M - 1);
-#pragma unroll
-      for (int q = 0; q < NR; ++q) {
-        const int k0 = 16 * q + 8 * h;
-        const uint4 ta = *reinterpret_cast<const uint4*>(tlr + (size_t)mt * r + k0);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int n = min(n0 + 32 * t + r32, N - 1);
-          const uint4 lb = *reinterpret_cast<const uint4*>(l2t + (size_t)n * r + k0);
-          acc[t] = mfma_bf16_32x32x16(as_v8bf(ta), as_v8bf(lb), acc[t]);
-        }
-      }
-    }
-
-    // Bias, bf16 rounding and the store. MFMA C/D layout: lane (r32, h), register v -> row
-    // 8 (v / 4) + 4 h + v % 4, column r32 of a 32 x 32 tile. The block's 128 x 128 bf16 tile goes
-    // through LDS (free after the last barrier) so that each lane stores 16 contiguous bytes.
-    uint16_t* tile = reinterpret_cast<uint16_t*>(lds);
-    __syncthreads();  // every wave has finished reading the stages
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = n0 + 32 * t + r32;
-      const float bv = (bias != nullptr && n < N) ? bf16_to_f32(bias[n]) : 0.0f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float o = acc[t][v] + bv;
-        if (gelu) o = gelu_tanh(o);
-        tile[(wrow + 8 * (v >> 2) + 4 * h + (v & 3)) * kEpiPitch + 32 * t + r32] = f32_to_bf16(o);
-      }
-    }
-    __syncthreads();
-    // Fused QKV (the structural-rewrite section of the Diffusers blog on Nunchaku Lite): the tile's
-    // 128 columns are one head (block-uniform part: 0 = Q, 1 = K, 2 = V). Q and K rows are RMS
-    // normalised per head and rotated pairwise; V passes unchanged.
-    const int qkv_part = qkv_heads > 0 ? n0 / (qkv_heads * kBN) : 2;
-    const float* norm_w = qkv_part == 0 ? q_norm_w : k_norm_w;
-    // 128 rows x 256 bytes: thread -> (row = 16 * pass + tid / 16, 16-byte chunk tid % 16)
-#pragma unroll
-    for (int pass = 0; pass < kBM / 16; ++pass) {
-      const int row = 16 * pass + (tid >> 4);
-      const int c8 = (tid & 15) * 8;
-      const int m = m0 + row;
-      const int n = n0 + c8;
-      uint4 v = *reinterpret_cast<const uint4*>(tile + row * kEpiPitch + c8);
-      if (qkv_part < 2) v = qk_norm_rope(v, norm_w, rope_cos, rope_sin, min(m, M - 1), c8);
-      // Y is written once and not read here: a non-temporal store keeps it from evicting the
-      // activation and weight tiles that other blocks on this XCD are still reading from L2.
-      if (m < M && n < N)
-        __builtin_nontemporal_store(__builtin_bit_cast(v4i, v), reinterpret_cast<v4i*>(y + (size_t)m * N + n));
-    }
-  }
-}
-
-template <int NR>
-hipError_t launch_nr(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw, const uint16_t* t,
-                     const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y, int M, int N, int K,
-                     const W4A4Epilogue& epi, hipStream_t stream) {
-  const int tiles_m = (M + kBM - 1) / kBM;
-  const int tiles_n = (N + kBN - 1) / kBN;
-  hipLaunchKernelGGL((w4a4_gemm_kernel<NR, false>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, qa, sa, qw,
-                     sw, t, l2t, r, bias, y, M, N, K, tiles_m, tiles_n, epi.gelu ? 1 : 0, epi.qkv_heads,
-                     epi.q_norm_w, epi.k_norm_w, epi.rope_cos, epi.rope_sin, nullptr, 0, 0, 0, 0);
-  return hipGetLastError();
-}
-
-}  // namespace
 
 hipError_t launch_w4a4_gemm(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                             const uint16_t* t, const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y,
                             int M, int N, int K, const W4A4Epilogue& epi, hipStream_t stream) {
-  switch (r / 16) {
-    case 0: return launch_nr<0>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 1: return launch_nr<1>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 2: return launch_nr<2>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 3: return launch_nr<3>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 4: return launch_nr<4>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 5: return launch_nr<5>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 6: return launch_nr<6>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 7: return launch_nr<7>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 8: return launch_nr<8>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 9: return launch_nr<9>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 10: return launch_nr<10>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 11: return launch_nr<11>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 12: return launch_nr<12>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 13: return launch_nr<13>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 14: return launch_nr<14>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 15: return launch_nr<15>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 16: return launch_nr<16>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    default: return hipErrorInvalidValue;
-  }
+  if (epi.gelu) return launch_w4a4_gemm_gelu(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+  if (epi.qkv_heads > 0)
+    return launch_w4a4_gemm_qkv(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+  return launch_epi<0>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
 }
 
 hipError_t launch_w4a4_group_sums(const uint8_t* qact, const uint8_t* qweight, int M, int N, int K, int m0, int n0,
@@ -451,9 +19,9 @@ hipError_t launch_w4a4_group_sums(const uint8_t* qact, const uint8_t* qweight, i
   const int tm0 = m0 / kBM, tm1 = (m0 + tm - 1) / kBM;
   const int tn0 = n0 / kBN, tn1 = (n0 + tn - 1) / kBN;
   const dim3 grid(tn1 - tn0 + 1, tm1 - tm0 + 1);
-  hipLaunchKernelGGL((w4a4_gemm_kernel<0, true>), grid, dim3(kThreads), 0, stream, qact, nullptr, qweight, nullptr,
-                     nullptr, nullptr, 0, nullptr, nullptr, M, N, K, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, out, m0,
-                     n0, tm, tn);
+  hipLaunchKernelGGL((w4a4_gemm_kernel<0, true, 0>), grid, dim3(kThreads), 0, stream, qact, nullptr, qweight,
+                     nullptr, nullptr, nullptr, 0, nullptr, nullptr, M, N, K, 0, 0, 0, nullptr, nullptr, nullptr, nullptr,
+                     out, m0, n0, tm, tn);
   return hipGetLastError();
 }
 

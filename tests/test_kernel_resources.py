@@ -28,9 +28,12 @@ def resources():
 
 def test_every_kernel_instantiation_reported(resources):
     count = lambda src: sum(1 for r in resources if r[0] == src)
-    # quantizer and GEMM: one instantiation per rank r = 16 q, q = 0..16 (+ the GEMM's debug dump)
+    # quantizer and GEMM: one instantiation per rank r = 16 q, q = 0..16 (+ the GEMM's debug dump);
+    # the GEMM's GELU and fused-QKV epilogues in their own units
     assert count("quant_act.hip") == 17
     assert count("w4a4_gemm.hip") == 18
+    assert count("w4a4_gemm_gelu.hip") == 17
+    assert count("w4a4_gemm_qkv.hip") == 17
     assert count("w4a16_gemv.hip") == 1
 
 
@@ -41,5 +44,5 @@ def test_no_kernel_uses_scratch(resources):
 
 def test_gemm_keeps_two_waves_per_simd(resources):
     for r in resources:
-        if r[0] == "w4a4_gemm.hip":
+        if r[0].startswith("w4a4_gemm"):
             assert r[5] >= 2, r
