@@ -13,7 +13,9 @@
 //     u = D * sw[g, n] - (1.5 * 2^23) * sw[g, n];     acc += u * sa[g, m]
 // and the common factor 1/256 is applied once at the end. The epilogue adds T L2 with bf16
 // MFMAs accumulating straight into the same float32 tile (C operand = acc), adds the bias and
-// stores bf16.
+// stores bf16. Two epilogue variants (a compile-time parameter): the tanh-form GELU before the
+// bf16 rounding (an MLP's up projection), and the per-head RMS norm + rotary embedding of the Q
+// and K columns of a fused QKV projection (a 128-column tile is one head).
 //
 // Tiling: block = 128 x 128 outputs, 4 waves stacked along M; wave tile 32 tokens x 128 columns
 // = 1 x 4 MFMA tiles of 32 x 32; two blocks per CU. One K step is one group of 64.
