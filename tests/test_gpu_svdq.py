@@ -285,6 +285,23 @@ def test_w4a4_gelu_parity(gpu, name):
     check_y(p, y_plain)
 
 
+@pytest.mark.parametrize("M,K,N,rank", [(33, 64, 48, 16), (77, 448, 144, 0), (130, 128, 272, 48)])
+def test_w4a4_gelu_small_shapes(gpu, M, K, N, rank):
+    """The GELU epilogue on ragged token counts, rank 0 and column counts that leave partial tiles."""
+    import torch
+    import quantized_gemm_amd as q
+    say(f"[w4a4 gelu shapes] M={M} K={K} N={N} r={rank}")
+    p = random_w4a4_problem(M, K, N, rank, seed=M + K + N + rank + 1)
+    layer = Layer(p, gpu)
+    qact, ascale, t = q.svdq_quantize_act(to_dev_bf16(p["x_bits"], gpu), layer.inv, layer.l1t)
+    y = q.svdq_linear_w4a4(qact, ascale, layer.qw, layer.sw, t, layer.l2t, layer.bias, activation="gelu_tanh")
+    torch.cuda.synchronize()
+    _, y_ref = oracle.svdq_linear_gelu(p["qa"], p["sa"], p["qw"], p["sw"], p["t"], p["l2"], p["bias"])
+    mx, mean = tolerance_report(bf16_to_np(y), y_ref)
+    say(f"  GELU(Y) max|err|/max|Y| = {mx:.3e}, mean rel = {mean:.3e}")
+    assert mx <= MAX_REL and mean <= MEAN_REL
+
+
 def test_mlp_pair_chained_on_real_intermediates(gpu):
     """Up projection with the fused GELU, then the down projection quantizing that output: the
     intermediate against the oracle's, and the down layer bit-exact (codes, scales) and within
