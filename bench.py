@@ -68,6 +68,8 @@ def parse():
                     help="time the up (+GELU) -> down MLP pair, GELU fused vs a separate GELU pass")
     ap.add_argument("--qkv-epilogue", action="store_true",
                     help="time the fused QKV projection with the Q/K norm + rotary epilogue vs torch after it")
+    ap.add_argument("--rank-sweep", action="store_true",
+                    help="time the quantizer and the GEMM of the QKV projection at ranks 0, 32, 128 and 256")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this size (a known-traffic "
                          "kernel that scales the HBM byte counters)")
@@ -448,6 +450,97 @@ def qkv_epilogue(args):
     print(json.dumps(out), flush=True)
 
 
+def rank_sweep(args):
+    """How the low-rank branch's cost grows with r on the fused QKV shape (M4608 K3072 N9216): the
+    quantizer (down projection fused) and the GEMM (T·L2 epilogue fused), each timed back to back
+    over rotating buffer sets, at r = 0 (the 4-bit product alone), 32, 128 and 256. The SVD of the
+    smoothed weight is computed once and truncated per rank."""
+    import torch
+    import synth
+    import quantized_gemm_amd as q
+    from quantized_gemm_amd import prep
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    q.load_library()
+    q.svdq_check_device()
+    cfg = synth.CONFIGS["qkv_r32"]
+    M, K, N = cfg.M, cfg.K, cfg.N
+    ranks = (0, 32, 128, 256)
+    log(f"[rank sweep] generating M={M} K={K} N={N}")
+    inp = synth.make_layer_inputs(cfg)
+    xf, wf = synth.f32_from_bf16_bits(inp["x"]), synth.f32_from_bf16_bits(inp["w"])
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    R = max(1, args.rotate)
+    xs = [bf16_dev(inp["x"]) for _ in range(R)]
+    bias_d = bf16_dev(inp["bias"])
+    qact = [torch.empty((K // 64, M, 32), dtype=torch.uint8, device=dev) for _ in range(R)]
+    asc = [torch.empty((K // 64, M), dtype=torch.float32, device=dev) for _ in range(R)]
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def timed(fn, n):
+        for s in range(min(n, 20)):
+            fn(s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for s in range(n):
+            fn(s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    n = max(1, args.steps)
+    svd, rows = None, []
+    for r in ranks:
+        log(f"[rank sweep] r={r}: decomposing and packing")
+        d = prep.decompose(xf, wf, r, svd=svd)
+        svd = d["svd"] if d["svd"] is not None else svd
+        qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, d["resid"])
+        inv = torch.from_numpy(d["inv_smooth"]).to(dev)
+        qw_d, sw_d = torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev)
+        if r:
+            l1t, l2t = q.svdq_pack_lowrank(d["l1"], d["l2"])
+            l1t_d, l2t_d = bf16_dev(l1t), bf16_dev(l2t)
+            tl = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        else:
+            l1t_d = l2t_d = None
+            tl = [None] * R
+
+        def quant(s, inv=inv, l1t_d=l1t_d, tl=tl):
+            k = s % R
+            q.svdq_quantize_act(xs[k], inv, l1t_d, qact[k], asc[k], tl[k], stream=sh)
+
+        def gemm(s, qw_d=qw_d, sw_d=sw_d, l2t_d=l2t_d, tl=tl):
+            k = s % R
+            q.svdq_linear_w4a4(qact[k], asc[k], qw_d, sw_d, tl[k], l2t_d, bias_d, ys[k], stream=sh)
+
+        quant(0)
+        torch.cuda.synchronize()
+        log(f"[rank sweep] r={r}: timing")
+        tq, tg = timed(quant, n), timed(gemm, n)
+        ops = 2.0 * M * N * K + 2.0 * M * r * (K + N)
+        rows.append({"rank": r, "quantize_act_us": round(tq, 2), "linear_w4a4_us": round(tg, 2),
+                     "layer_us": round(tq + tg, 2), "gemm_tops": round(ops / (tg * 1e-6) / 1e12, 1)})
+        del quant, gemm, tl, qw_d, sw_d, l1t_d, l2t_d
+    base = rows[0]
+    for row in rows:
+        row["low_rank_cost"] = round(row["layer_us"] / base["layer_us"] - 1.0, 4)
+    out = {
+        "metric": f"cost of the fused low-rank branch against its rank (QKV projection M{M} K{K} N{N})",
+        "unit": "us",
+        "steps": n,
+        "config": {"workload": f"svdq_w4a4 qkv M{M} K{K} N{N} r0/32/128/256", "rotating_buffer_sets": R},
+        "ranks": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -463,6 +556,9 @@ def main():
         return
     if args.qkv_epilogue:
         qkv_epilogue(args)
+        return
+    if args.rank_sweep:
+        rank_sweep(args)
         return
 
     import torch

@@ -25,11 +25,12 @@ def _bf16_values(a: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).reshape(np.shape(a))
 
 
-def decompose(x_calib: np.ndarray, w: np.ndarray, rank: int) -> Dict[str, np.ndarray]:
+def decompose(x_calib: np.ndarray, w: np.ndarray, rank: int, svd=None) -> Dict[str, np.ndarray]:
     """x_calib float32 [M, K] (calibration activations), w float32 [K, N] (y = x @ w).
 
     Returns ``inv_smooth`` float32 [K], ``l1`` float32 [K, r] and ``l2`` float32 [r, N] (bf16-exact
-    values), ``resid`` float32 [K, N].
+    values), ``resid`` float32 [K, N], and ``svd``: the (u, s, vt) of the smoothed weight, which a
+    later call on the same x_calib and w may pass back in to get another rank without a new SVD.
     """
     xa = np.abs(np.asarray(x_calib, dtype=np.float64)).max(axis=0)
     wa = np.abs(np.asarray(w, dtype=np.float64)).max(axis=1)
@@ -38,7 +39,9 @@ def decompose(x_calib: np.ndarray, w: np.ndarray, rank: int) -> Dict[str, np.nda
     w_hat = (1.0 / inv.astype(np.float64))[:, None] * np.asarray(w, dtype=np.float64)
     K, N = w_hat.shape
     if rank > 0:
-        u, s, vt = np.linalg.svd(w_hat, full_matrices=False)
+        if svd is None:
+            svd = np.linalg.svd(w_hat, full_matrices=False)
+        u, s, vt = svd
         l1 = _bf16_values((u[:, :rank] * s[:rank]).astype(np.float32))
         l2 = _bf16_values(vt[:rank].astype(np.float32))
         resid = (w_hat - l1.astype(np.float64) @ l2.astype(np.float64)).astype(np.float32)
@@ -46,4 +49,4 @@ def decompose(x_calib: np.ndarray, w: np.ndarray, rank: int) -> Dict[str, np.nda
         l1 = np.zeros((K, 0), np.float32)
         l2 = np.zeros((0, N), np.float32)
         resid = w_hat.astype(np.float32)
-    return {"inv_smooth": inv, "l1": l1, "l2": l2, "resid": resid}
+    return {"inv_smooth": inv, "l1": l1, "l2": l2, "resid": resid, "svd": svd}

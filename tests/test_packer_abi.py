@@ -154,6 +154,20 @@ def test_product_prep_matches_oracle_prep():
     assert np.array_equal(p["resid"], d["resid"])
 
 
+def test_product_prep_reuses_the_svd_across_ranks():
+    from quantized_gemm_amd import prep
+    cfg = synth.CONFIGS["tiny"]
+    inp = synth.make_layer_inputs(cfg)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    first = prep.decompose(x, w, 32)
+    for r in (16, 48):
+        fresh, reused = prep.decompose(x, w, r), prep.decompose(x, w, r, svd=first["svd"])
+        for key in ("inv_smooth", "l1", "l2", "resid"):
+            assert np.array_equal(fresh[key], reused[key]), (r, key)
+    assert prep.decompose(x, w, 0)["svd"] is None
+
+
 # ---------------------------------------------------------------------------------------------
 # argument validation (checked before any HIP call, so it runs without a GPU)
 # ---------------------------------------------------------------------------------------------
