@@ -389,6 +389,20 @@ def test_qkv_norm_rope_small_ragged(gpu):
     assert mx <= MAX_REL and mean <= MEAN_REL
 
 
+# (M, K, heads, rank): one token and one head with no low-rank branch, a ragged token count with a
+# rank between instantiation steps, and the largest rank with a partial last row tile
+@pytest.mark.parametrize("M,K,heads,rank", [(1, 64, 1, 0), (77, 448, 1, 48), (130, 320, 3, 256)])
+def test_qkv_norm_rope_ranks_and_ragged_tokens(gpu, M, K, heads, rank):
+    say(f"[qkv] M={M} K={K} heads={heads} r={rank}")
+    p = random_w4a4_problem(M, K, 3 * heads * 128, rank, seed=94 + rank)
+    tables = _qkv_tables(M, heads, seed=95 + rank)
+    y, y_plain = _run_qkv(gpu, Layer(p, gpu), p["x_bits"], heads, tables)
+    _check_qkv_epilogue(y, y_plain, heads, tables)
+    mx, mean = tolerance_report(y, oracle.qkv_norm_rope(p["y"], heads, *tables))
+    say(f"  QKV max|err|/max|ref| = {mx:.3e}, mean rel = {mean:.3e}")
+    assert mx <= MAX_REL and mean <= MEAN_REL
+
+
 @pytest.mark.timeout(600)
 def test_qkv_norm_rope_flux_shape(gpu):
     """FLUX attention: M 4608, K 3072, 24 heads of 128 (N 9216), rank 32."""
