@@ -525,8 +525,15 @@ def rank_sweep(args):
         log(f"[rank sweep] r={r}: timing")
         tq, tg = timed(quant, n), timed(gemm, n)
         ops = 2.0 * M * N * K + 2.0 * M * r * (K + N)
-        rows.append({"rank": r, "quantize_act_us": round(tq, 2), "linear_w4a4_us": round(tg, 2),
-                     "layer_us": round(tq + tg, 2), "gemm_tops": round(ops / (tg * 1e-6) / 1e12, 1)})
+        row = {"rank": r, "quantize_act_us": round(tq, 2), "linear_w4a4_us": round(tg, 2),
+               "layer_us": round(tq + tg, 2), "gemm_tops": round(ops / (tg * 1e-6) / 1e12, 1)}
+        if r:
+            # context for the fused down projection: the same product unfused, X (bf16) @ (inv * L1)
+            # in torch (rocBLAS/hipBLASLt), which the unfused layer would add to the r = 0 quantizer
+            l1s = torch.from_numpy(d["inv_smooth"][:, None].astype(np.float64) * d["l1"]).to(dev).to(torch.bfloat16)
+            row["down_projection_torch_us"] = round(timed(lambda s: torch.matmul(xs[s % R], l1s), n), 2)
+            del l1s
+        rows.append(row)
         del quant, gemm, tl, qw_d, sw_d, l1t_d, l2t_d
     base = rows[0]
     for row in rows:
