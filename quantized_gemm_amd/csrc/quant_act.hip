@@ -111,6 +111,12 @@ constexpr int kQaAhead = 3;       // groups in flight ahead of the computation
 constexpr int kRedCols = 4;       // rank tiles of 16 columns per step of the T reduction
 constexpr int kTPitch = 128 + 16;  // bytes per token row of a wave's bf16 operand slice
 
+// X is read exactly once: its loads are marked non-temporal, so the stream of X lines does not
+// evict the L1 operand that every block re-reads from L2.
+__device__ __forceinline__ uint4 load_x16(const uint16_t* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p)));
+}
+
 template <int NR>
 __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                      const float* __restrict__ inv,
@@ -218,15 +224,15 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
       load_inv(gc, ivc);
 #pragma unroll
       for (int q = 0; q < kQaAhead; ++q) {
-        px[q][0] = *reinterpret_cast<const uint4*>(xr0 + (gc + q) * kGroup);
-        px[q][1] = *reinterpret_cast<const uint4*>(xr1 + (gc + q) * kGroup);
+        px[q][0] = load_x16(xr0 + (gc + q) * kGroup);
+        px[q][1] = load_x16(xr1 + (gc + q) * kGroup);
       }
 #pragma unroll
       for (int q = 0; q < kQaChunk; ++q) {
         if (q + 1 < kQaChunk) load_inv(gc + q + 1, ivn);
         if (q + kQaAhead < kQaChunk) {
-          px[q + kQaAhead][0] = *reinterpret_cast<const uint4*>(xr0 + (gc + q + kQaAhead) * kGroup);
-          px[q + kQaAhead][1] = *reinterpret_cast<const uint4*>(xr1 + (gc + q + kQaAhead) * kGroup);
+          px[q + kQaAhead][0] = load_x16(xr0 + (gc + q + kQaAhead) * kGroup);
+          px[q + kQaAhead][1] = load_x16(xr1 + (gc + q + kQaAhead) * kGroup);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep this issue order: the scheduler would sink the loads
         process(px[q][0], px[q][1], ivc, gc + q);
@@ -238,8 +244,8 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
 #pragma unroll
       for (int q = 0; q < kQaChunk; ++q) {
         const int e = min(gc + q, g_end - 1) * kGroup;
-        px[q][0] = *reinterpret_cast<const uint4*>(xr0 + e);
-        px[q][1] = *reinterpret_cast<const uint4*>(xr1 + e);
+        px[q][0] = load_x16(xr0 + e);
+        px[q][1] = load_x16(xr1 + e);
       }
 #pragma unroll
       for (int q = 0; q < kQaChunk; ++q) {

@@ -64,7 +64,9 @@ __device__ __forceinline__ void load_tile(TileLoad& tl, const uint8_t* __restric
     // in the upper half for odd L; the compute picks them.
     const bool paired = g + 1 < G;
     const int off = paired ? 16 * lane : 16 * (lane >> 1);
-    tl.w[p] = *reinterpret_cast<const uint4*>(tile + (size_t)g * 512 + off);
+    // each weight byte is read once: non-temporal, so the stream does not evict X from L2
+    tl.w[p] = __builtin_bit_cast(
+        uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i*>(tile + (size_t)g * 512 + off)));
   }
 #pragma unroll
   for (int q = 0; q < kAwqPer; ++q) tl.s[q] = scales[(size_t)min(gb + q, G - 1) * N + t * 16 + i];
