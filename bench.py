@@ -10,10 +10,16 @@ its activations / W4A16 weights from HBM rather than the 256 MB Infinity Cache.
 
 Prints one JSON line. ``value`` = algorithmic operations of the step / step time, in TOPS
 (int8-MFMA ops 2MNK of (b) + bf16 low-rank flops 2Mr(K+N) + W4A16 flops 2MNK of (c)).
-``roofline`` covers the dominant kernel (b): 2MNK / its average launch time, measured with HIP
-events on the launch stream around the GEMM of every 10th timed step (every recorded event adds a
-few microseconds to its step, so the other steps carry none), against the MI355X dense int8 MFMA
-peak. The per-kernel rates of (a) and (c) are measured after the timed region, each kernel alone.
+``roofline`` covers the dominant kernel (b): 2MNK / its median launch time, against the MI355X
+dense int8 MFMA peak. The timed region holds no event; after it, ``--gemm-samples`` more steps
+(default 200) each bracket their GEMM with HIP events on the launch stream, so the GEMM is sampled
+in the same context as in the timed steps. The per-kernel rates of (a) and (c), and the GEMM
+alone, are measured after that, each kernel back to back over the rotating buffers.
+
+``--all-configs`` reports every configuration (attn, up, down, QKV at r = 32/128/256, W4A16) and
+the unit microbenchmarks (pure matrix-core and vector rates at the observed clock);
+``--unit-peaks`` only the microbenchmarks; ``--only gemm|quant|awq`` launches one kernel of the
+default workload ``--steps`` times (for hardware-counter runs).
 
 ``--naive-vs-fused`` instead measures the engine-design figure's panel (a) claim on this GPU (a
 rank-32 low-rank branch run naively, with a separate down projection that reads the 16-bit input
@@ -60,8 +66,6 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4608, help="token rows in the CPU-oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the oracle sample for this long")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="bracket the GEMM of every N-th timed step with HIP events")
     ap.add_argument("--naive-vs-fused", action="store_true",
                     help="time the 4-bit branch alone, the naive unfused low-rank branch and the fused kernels")
     ap.add_argument("--mlp-pair", action="store_true",
@@ -70,6 +74,15 @@ def parse():
                     help="time the fused QKV projection with the Q/K norm + rotary epilogue vs torch after it")
     ap.add_argument("--rank-sweep", action="store_true",
                     help="time the quantizer and the GEMM of the QKV projection at ranks 0, 32, 128 and 256")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="per-configuration throughput: quantizer, GEMM and layer of attn, up, down and the QKV "
+                         "rank sweep (r32/128/256), the W4A16 projection, and the unit peaks at the observed clock")
+    ap.add_argument("--unit-peaks", action="store_true",
+                    help="only the execution-unit microbenchmarks (int8/bf16/f32 matrix core, f32 vector FMA)")
+    ap.add_argument("--only", choices=["gemm", "quant", "awq"], default=None,
+                    help="launch one kernel of the default workload --steps times back to back (for counter runs)")
+    ap.add_argument("--gemm-samples", type=int, default=200,
+                    help="steps after the timed region whose GEMM is bracketed by HIP events (roofline samples)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this size (a known-traffic "
                          "kernel that scales the HBM byte counters)")
@@ -139,6 +152,64 @@ def cpu_baseline(cfg, awq_cfg, rows: int, seconds: float):
             "sample": f"{rows} of {cfg.M} tokens of the {cfg.name} layer (activation quantization, float64 "
                       f"dequantized product, low-rank, bias) + the full W4A16 projection M={awq_cfg.M}, "
                       f"{passes} passes, mean"}
+
+
+def batch_timing(fn, stream, launches=200, batches=10, warm=20):
+    """Per-launch time (us) of ``fn(s)`` run back to back: ``warm`` untimed launches, then
+    ``launches`` launches in ``batches`` equal batches, each between two HIP events on ``stream``;
+    the statistics are over the batch means."""
+    import torch
+    for s in range(warm):
+        fn(s)
+    per = max(1, launches // batches)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(batches)]
+    torch.cuda.synchronize()
+    k = 0
+    for a, b in evs:
+        a.record(stream)
+        for _ in range(per):
+            fn(k)
+            k += 1
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) / per * 1e3 for a, b in evs])
+    return {"median": round(float(np.median(t)), 2), "min": round(float(t.min()), 2),
+            "max": round(float(t.max()), 2), "mean": round(float(t.mean()), 2), "launches": per * batches}
+
+
+def unit_peaks(dev, stream):
+    """Matrix-core and vector rates of this GPU from the microbenchmarks of include/svdq_bench.h:
+    achieved rate, the shader clock it ran at (s_memtime / s_memrealtime), and the rate per CU and
+    clock, for the int8 and bf16 matrix shapes, the float32 outer-product shape and the float32
+    vector FMA."""
+    import torch
+    import quantized_gemm_amd as q
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    blocks = 4 * cus
+    clocks = torch.zeros((blocks, 2), dtype=torch.int64, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    out = {"compute_units": cus}
+    for kind, (_, ops_per_inst) in q.SVDQ_BENCH_KINDS.items():
+        iters = 4000 if kind == "mfma_i8_32x32x32" else 2000
+        insts_per_iter = 64 if kind == "valu_fma_f32" else 16
+        q.svdq_bench_unit_peak(kind, blocks, 10, clocks, sink, stream=stream)  # warm
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        q.svdq_bench_unit_peak(kind, blocks, iters, clocks, sink, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3
+        ops = float(blocks) * 4 * iters * insts_per_iter * ops_per_inst
+        ck = clocks.cpu().numpy().astype(np.float64)
+        ghz = float(np.median(ck[:, 0] / np.maximum(ck[:, 1], 1) * 0.1))
+        rate = ops / t / 1e12
+        out[kind] = {"T_per_s": round(rate, 2), "clock_GHz": round(ghz, 3),
+                     "ops_per_clk_per_CU": round(rate * 1e12 / (ghz * 1e9) / cus, 1),
+                     "cycles_per_wave_instruction": round(ghz * 1e9 * t / (iters * insts_per_iter * blocks * 4 /
+                                                                          (4 * cus)), 2)}
+    return out
 
 
 def naive_low_rank_layer(q, x, inv, l1s, l2, qw, sw, bias, qact, asc, y, stream=None):
@@ -548,6 +619,134 @@ def rank_sweep(args):
     print(json.dumps(out), flush=True)
 
 
+def quant_bytes(M, K, r):
+    """Algorithmic bytes of kernel (a): X, codes, scales, T, the L1 operand and the smoothing vector."""
+    return M * K * 2 + M * K // 2 + (K // 64) * M * 4 + M * r * 2 + r * K * 2 + K * 4
+
+
+def gemm_bytes(M, K, N, r):
+    """Algorithmic bytes of kernel (b): both code matrices, both scale arrays, T, L2, bias and Y."""
+    return M * K // 2 + N * K // 2 + (K // 64) * (M + N) * 4 + M * r * 2 + N * r * 2 + N * 2 + M * N * 2
+
+
+def awq_bytes(M, K, N):
+    return N * K // 2 + (K // 64) * N * 2 + M * K * 2 + M * N * 2
+
+
+def all_configs(args):
+    """Throughput of every W4A4 configuration (attn, up, down, the QKV projection at r = 32, 128,
+    256) and of the W4A16 projection, each kernel timed alone back to back over rotating buffer
+    sets (10 batches of launches between HIP events; median, min and max of the batch means), and
+    the layer (quantizer + GEMM alternating). Also the unit microbenchmarks, so that the GEMM is
+    reported against both the published int8 peak and the matrix-core rate measured at the clock
+    this GPU ran at."""
+    import torch
+    import synth
+    import quantized_gemm_amd as q
+    from quantized_gemm_amd import prep
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    q.load_library()
+    q.svdq_check_device()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    n = max(20, args.steps)
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    log("[all] unit microbenchmarks")
+    peaks = unit_peaks(dev, stream)
+    i8 = peaks["mfma_i8_32x32x32"]
+    rows = []
+    svd_cache = {}
+    for name, r in (("attn", 32), ("up", 32), ("down", 32), ("qkv_r32", 32), ("qkv_r32", 128), ("qkv_r32", 256)):
+        cfg = synth.CONFIGS[name].with_rank(r) if name.startswith("qkv") else synth.CONFIGS[name]
+        M, K, N = cfg.M, cfg.K, cfg.N
+        log(f"[all] {cfg.name}: M={M} K={K} N={N} r={r}: preparing")
+        base = name
+        if base not in svd_cache:
+            svd_cache.clear()
+            inp = synth.make_layer_inputs(cfg)
+            svd_cache[base] = (inp, synth.f32_from_bf16_bits(inp["x"]), synth.f32_from_bf16_bits(inp["w"]), None)
+        inp, xf, wf, svd = svd_cache[base]
+        d = prep.decompose(xf, wf, r, svd=svd)
+        svd_cache[base] = (inp, xf, wf, d["svd"])
+        qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, d["resid"])
+        l1t, l2t = q.svdq_pack_lowrank(d["l1"], d["l2"])
+        ba, bb = quant_bytes(M, K, r), gemm_bytes(M, K, N, r)
+        R = int(min(16, max(4, -(-600_000_000 // ba))))
+        xs = [bf16_dev(inp["x"]) for _ in range(R)]
+        inv = torch.from_numpy(d["inv_smooth"]).to(dev)
+        qw_d, sw_d, l1t_d, l2t_d = (torch.from_numpy(qw).to(dev), torch.from_numpy(sw).to(dev), bf16_dev(l1t),
+                                    bf16_dev(l2t))
+        bias_d = bf16_dev(inp["bias"])
+        qact = [torch.empty((K // 64, M, 32), dtype=torch.uint8, device=dev) for _ in range(R)]
+        asc = [torch.empty((K // 64, M), dtype=torch.float32, device=dev) for _ in range(R)]
+        tl = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def quant(s):
+            k = s % R
+            q.svdq_quantize_act(xs[k], inv, l1t_d, qact[k], asc[k], tl[k], stream=sh)
+
+        def gemm(s):
+            k = s % R
+            q.svdq_linear_w4a4(qact[k], asc[k], qw_d, sw_d, tl[k], l2t_d, bias_d, y, stream=sh)
+
+        def layer(s):
+            quant(s)
+            gemm(s)
+
+        for s in range(R):
+            quant(s)
+        torch.cuda.synchronize()
+        log(f"[all] {cfg.name}: timing")
+        tq = batch_timing(quant, stream, n)
+        tg = batch_timing(gemm, stream, n)
+        tlr = batch_timing(layer, stream, n)
+        ops = 2.0 * M * N * K
+        lr = 2.0 * M * r * (K + N)
+        rows.append({
+            "config": cfg.name, "M": M, "K": K, "N": N, "rank": r, "rotating_buffer_sets": R,
+            "quantize_act_us": tq, "quantize_act_GBs": round(ba / (tq["median"] * 1e-6) / 1e9, 1),
+            "quantize_act_hbm_frac": round(ba / (tq["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "linear_w4a4_us": tg, "linear_w4a4_TOPS": round(ops / (tg["median"] * 1e-6) / 1e12, 1),
+            "linear_w4a4_frac_int8_peak": round(ops / (tg["median"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4),
+            "linear_w4a4_frac_measured_mfma": round(ops / (tg["median"] * 1e-6) / 1e12 / i8["T_per_s"], 4),
+            "linear_w4a4_lowrank_GFLOP": round(lr / 1e9, 3),
+            "linear_w4a4_alg_bytes": bb,
+            "layer_us": tlr, "layer_TOPS": round((ops + lr) / (tlr["median"] * 1e-6) / 1e12, 1),
+        })
+        log(f"[all] {json.dumps(rows[-1])}")
+        del xs, qact, asc, tl, y, qw_d, sw_d, l1t_d, l2t_d
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    acfg = synth.CONFIGS["awq"]
+    ainp = synth.make_layer_inputs(acfg)
+    aqw, ascl = q.svdq_pack_weights(q.SVDQ_FMT_W4A16_BF16SCALE, synth.f32_from_bf16_bits(ainp["w"]))
+    bc = awq_bytes(acfg.M, acfg.K, acfg.N)
+    R = int(min(32, max(4, -(-600_000_000 // bc))))
+    ax = bf16_dev(ainp["x"])
+    aqws = [torch.from_numpy(aqw).to(dev) for _ in range(R)]
+    ascls = [bf16_dev(ascl) for _ in range(R)]
+    ay = torch.empty((acfg.M, acfg.N), dtype=torch.bfloat16, device=dev)
+    log("[all] awq: timing")
+    tc = batch_timing(lambda s: q.awq_linear_w4a16(ax, aqws[s % R], ascls[s % R], None, ay, stream=sh), stream,
+                      max(n, 500))
+    awq = {"config": "awq", "M": acfg.M, "K": acfg.K, "N": acfg.N, "rotating_buffer_sets": R,
+           "awq_linear_w4a16_us": tc, "GBs": round(bc / (tc["median"] * 1e-6) / 1e9, 1),
+           "hbm_frac": round(bc / (tc["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bc}
+    out = {"metric": "per-configuration throughput of the SVDQuant W4A4 + low-rank layer and the W4A16 projection",
+           "unit_peaks": peaks, "int8_peak_published_TOPS": INT8_PEAK_TOPS, "hbm_peak_GBs": HBM_PEAK_GBS,
+           "w4a4": rows, "w4a16": awq,
+           "timing": "each kernel alone, back to back over rotating buffer sets; 10 batches between HIP events, "
+                     "median / min / max / mean of the batch means (us per launch)"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -566,6 +765,17 @@ def main():
         return
     if args.rank_sweep:
         rank_sweep(args)
+        return
+    if args.all_configs:
+        all_configs(args)
+        return
+    if args.unit_peaks:
+        import torch
+        import quantized_gemm_amd as q
+        assert torch.cuda.is_available(), "bench.py needs a HIP device"
+        q.load_library()
+        q.svdq_check_device()
+        print(json.dumps({"unit_peaks": unit_peaks(torch.device("cuda:0"), torch.cuda.current_stream())}), flush=True)
         return
 
     import torch
@@ -626,6 +836,21 @@ def main():
             ev[1].record(stream)
         q.awq_linear_w4a16(ax, aqws[k], ascl_d, None, ay, stream=sh)
 
+    if args.only is not None:
+        # one kernel of the step, --steps launches back to back (inputs from one pass of the step)
+        step(0)
+        torch.cuda.synchronize()
+        fn = {"gemm": lambda s: q.svdq_linear_w4a4(qact[s % R], asc[s % R], qw_d, sw_d, tl[s % R], l2t_d, bias_d, y,
+                                                   stream=sh),
+              "quant": lambda s: q.svdq_quantize_act(xs[s % R], inv, l1t_d, qact[s % R], asc[s % R], tl[s % R],
+                                                     stream=sh),
+              "awq": lambda s: q.awq_linear_w4a16(ax, aqws[s % R], ascl_d, None, ay, stream=sh)}[args.only]
+        for s in range(R):
+            step(s)
+        t = batch_timing(fn, stream, args.steps, batches=max(1, min(10, args.steps)), warm=args.warmup)
+        print(json.dumps({"only": args.only, "us": t}), flush=True)
+        return
+
     log(f"[bench] warmup {args.warmup}")
     for s in range(args.warmup):
         step(s)
@@ -640,41 +865,37 @@ def main():
         log(f"[bench] copy calibration: {n} bytes read, {n} bytes written")
         del src, dst
 
-    # Timed region: exactly K steps, synchronised on both sides. Every EVERY-th step brackets the
-    # W4A4 GEMM (the dominant kernel) with HIP events on its stream; each recorded event costs the
-    # step a few microseconds, so the other steps carry none.
-    every = max(1, args.event_every)
-    sampled = list(range(0, args.steps, every))
-    evs = {s: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for s in sampled}
+    # Timed region: exactly K steps, synchronised on both sides, with no event inside it.
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     start.record(stream)
     for s in range(args.steps):
-        step(s, evs.get(s))
+        step(s)
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    t_b = float(np.mean([e[0].elapsed_time(e[1]) for e in evs.values()]))
 
-    # Per-kernel rates of the two HBM-bound kernels (outside the timed region): each kernel alone,
-    # back to back over the rotating buffers, between two events.
-    def isolated(fn, n=200):
-        for s in range(20):
-            fn(s)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for s in range(n):
-            fn(s)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n
+    # Roofline samples of the dominant kernel (after the timed region): more steps of the same
+    # workload, each with its GEMM between two HIP events on the launch stream, so the GEMM runs
+    # in the same context (alternating with the memory-bound kernels) as in the timed steps.
+    ns = max(20, args.gemm_samples)
+    log(f"[bench] {ns} GEMM samples")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ns)]
+    torch.cuda.synchronize()
+    for s in range(ns):
+        step(args.steps + s, evs[s])
+    torch.cuda.synchronize()
+    tb_samples = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    t_b = float(np.median(tb_samples)) * 1e-3  # ms
 
-    t_a = isolated(lambda s: q.svdq_quantize_act(xs[s % R], inv, l1t_d, qact[s % R], asc[s % R], tl[s % R],
-                                                 stream=sh))
-    t_c = isolated(lambda s: q.awq_linear_w4a16(ax, aqws[s % R], ascl_d, None, ay, stream=sh))
+    # Per-kernel rates, each kernel alone, back to back over the rotating buffers.
+    t_a = batch_timing(lambda s: q.svdq_quantize_act(xs[s % R], inv, l1t_d, qact[s % R], asc[s % R], tl[s % R],
+                                                     stream=sh), stream)
+    t_c = batch_timing(lambda s: q.awq_linear_w4a16(ax, aqws[s % R], ascl_d, None, ay, stream=sh), stream, 500)
+    t_b_alone = batch_timing(lambda s: q.svdq_linear_w4a4(qact[s % R], asc[s % R], qw_d, sw_d, tl[s % R], l2t_d,
+                                                          bias_d, y, stream=sh), stream)
 
     gemm_ops = 2.0 * M * N * K
     lr_flops = 2.0 * M * r * (K + N)
@@ -682,10 +903,12 @@ def main():
     step_ops = gemm_ops + lr_flops + awq_flops
     value = step_ops / (ms_step * 1e-3) / 1e12
     achieved_b = gemm_ops / (t_b * 1e-3) / 1e12
-    bytes_a = M * K * 2 + M * K // 2 + (K // 64) * M * 4 + M * r * 2 + (r * K * 2) + K * 4
-    bytes_c = awq_cfg.N * awq_cfg.K // 2 + (awq_cfg.K // 64) * awq_cfg.N * 2 + awq_cfg.M * awq_cfg.K * 2 + \
-        awq_cfg.M * awq_cfg.N * 2
+    bytes_a = quant_bytes(M, K, r)
+    bytes_c = awq_bytes(awq_cfg.M, awq_cfg.K, awq_cfg.N)
     traffic = load_traffic("w4a4_gemm.hip", cfg.name)
+
+    def rate(nbytes, us):
+        return round(nbytes / (us * 1e-6) / 1e9, 1)
 
     out = {
         "metric": METRIC,
@@ -705,19 +928,24 @@ def main():
                    "awq": [awq_cfg.M, awq_cfg.K, awq_cfg.N], "rotating_buffer_sets": R},
         "roofline": {"bound": "mfma", "achieved": round(achieved_b, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_b / INT8_PEAK_TOPS, 4), "traffic": traffic,
-                     "kernel": "w4a4_gemm_kernel (svdq_linear_w4a4)", "ops_per_launch": gemm_ops},
+                     "kernel": "w4a4_gemm_kernel (svdq_linear_w4a4)", "ops_per_launch": gemm_ops,
+                     "samples": int(len(tb_samples)), "us_median": round(float(np.median(tb_samples)), 2),
+                     "us_min": round(float(tb_samples.min()), 2), "us_max": round(float(tb_samples.max()), 2)},
         "kernels": {
-            "svdq_quantize_act_us": round(t_a * 1e3, 2),
-            "svdq_quantize_act_GBs": round(bytes_a / (t_a * 1e-3) / 1e9, 1),
-            "svdq_quantize_act_hbm_frac": round(bytes_a / (t_a * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "svdq_quantize_act_us": t_a["median"],
+            "svdq_quantize_act_GBs": rate(bytes_a, t_a["median"]),
+            "svdq_quantize_act_hbm_frac": round(rate(bytes_a, t_a["median"]) / HBM_PEAK_GBS, 4),
             "svdq_linear_w4a4_us": round(t_b * 1e3, 2),
             "svdq_linear_w4a4_TOPS": round(achieved_b, 2),
-            "awq_linear_w4a16_us": round(t_c * 1e3, 2),
-            "awq_linear_w4a16_GBs": round(bytes_c / (t_c * 1e-3) / 1e9, 1),
-            "awq_linear_w4a16_hbm_frac": round(bytes_c / (t_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "layer_TOPS_a_plus_b": round(gemm_ops / ((t_a + t_b) * 1e-3) / 1e12, 2),
-            "timing": f"GEMM: HIP events around every {every}-th timed step ({len(evs)} samples); "
-                      "quantizer and W4A16: each alone, back to back, 200 launches",
+            "svdq_linear_w4a4_alone_us": t_b_alone["median"],
+            "awq_linear_w4a16_us": t_c["median"],
+            "awq_linear_w4a16_GBs": rate(bytes_c, t_c["median"]),
+            "awq_linear_w4a16_hbm_frac": round(rate(bytes_c, t_c["median"]) / HBM_PEAK_GBS, 4),
+            "layer_TOPS_a_plus_b": round(gemm_ops / ((t_a["median"] * 1e-3 + t_b) * 1e-3) / 1e12, 2),
+            "timing": f"GEMM: HIP events around the GEMM of {len(tb_samples)} steps after the timed region "
+                      f"(median); '_alone': the GEMM back to back; quantizer and W4A16: each alone, back to back "
+                      f"over the rotating buffers, 10 batches (median of the batch means)",
+            "batches": {"quantize_act": t_a, "linear_w4a4_alone": t_b_alone, "awq_linear_w4a16": t_c},
         },
     }
     if not args.no_cpu_baseline:

@@ -39,6 +39,7 @@ _SIGNATURES = {
                                     _vp, _vp, _vp]),
     "awq_linear_w4a16": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "svdq_debug_group_sums": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp]),
+    "svdq_bench_unit_peak": (_int, [_int, _int, _int, _vp, _vp, _vp]),
 }
 
 
@@ -265,8 +266,12 @@ def svdq_debug_group_sums(qact, qweight, N: int, m0: int, n0: int, tm: int, tn: 
     """Exact per-group integer sums P[g, m0+i, n0+j] of the W4A4 product: int32 [K/64, tm, tn].
     qact uint8 [K/64, M, 32]."""
     import torch
+    if qact.dim() != 3 or qact.shape[2] != 32:
+        raise ValueError(f"qact must be [K/64, M, 32], got {tuple(qact.shape)}")
     G, M, _ = qact.shape
     K = G * GROUP
+    if qweight.numel() != N * K // 2:
+        raise ValueError("qweight size does not match [N, K/2]")
     if out is None:
         out = torch.empty((K // GROUP, tm, tn), dtype=torch.int32, device=qact.device)
     st = load_library().svdq_debug_group_sums(
@@ -274,3 +279,19 @@ def svdq_debug_group_sums(qact, qweight, N: int, m0: int, n0: int, tm: int, tn: 
         _dev_ptr(out, "out", (torch.int32,), (K // GROUP, tm, tn)), _stream(stream))
     _check("svdq_debug_group_sums", st)
     return out
+
+
+SVDQ_BENCH_KINDS = {"mfma_i8_32x32x32": (0, 2 * 32 * 32 * 32), "mfma_bf16_32x32x16": (1, 2 * 32 * 32 * 16),
+                    "mfma_f32_32x32x1_2b": (2, 2 * 2 * 32 * 32), "valu_fma_f32": (3, 2 * 64)}
+
+
+def svdq_bench_unit_peak(kind: str, blocks: int, iters: int, clocks, sink, stream=None) -> None:
+    """Launch the unit microbenchmark (include/svdq_bench.h): clocks uint64-compatible int64
+    device tensor [blocks, 2], sink int32 device tensor [256]."""
+    import torch
+    code = SVDQ_BENCH_KINDS[kind][0]
+    st = load_library().svdq_bench_unit_peak(code, int(blocks), int(iters),
+                                             _dev_ptr(clocks, "clocks", (torch.int64,), (blocks, 2)),
+                                             _dev_ptr(sink, "sink", (torch.int32,), (256,)), _stream(stream))
+    if st != 0:
+        raise RuntimeError(f"svdq_bench_unit_peak failed with {st}")

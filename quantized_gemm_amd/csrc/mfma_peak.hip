@@ -1,0 +1,122 @@
+// Microbenchmarks of the gfx950 execution units that bound the SVDQuant kernels: the dense int8
+// matrix-core rate (the denominator of the W4A4 product's roofline), the bf16 and float32 matrix
+// shapes used by the low-rank epilogue and the rescale, and the float32 vector FMA rate.
+//
+// Each kernel keeps four independent accumulator chains per wave (no dependent-issue stalls),
+// touches no memory in its loop, and records per block the elapsed shader clock (s_memtime) and
+// real-time counter (s_memrealtime, 100 MHz), so the caller derives both the achieved rate and
+// the clock the chip ran at while it ran.
+#include "../../include/svdq_bench.h"
+#include "svdq_device.h"
+
+namespace svdq {
+namespace {
+
+constexpr int kUnroll = 4;
+
+template <int KIND>
+__global__ __launch_bounds__(256) void peak_kernel(int iters, unsigned long long* __restrict__ clk,
+                                                   int* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  float fsum = 0.0f;
+  int isum = 0;
+  if constexpr (KIND == SVDQ_BENCH_MFMA_I8_32X32X32) {
+    const v4i a = {lane, lane * 3, lane * 5, lane * 7};
+    const v4i b = {lane * 11, lane * 13, lane * 17, lane * 19};
+    v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c3, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) isum += c0[v] ^ c1[v] ^ c2[v] ^ c3[v];
+  } else if constexpr (KIND == SVDQ_BENCH_MFMA_BF16_32X32X16) {
+    const v8bf a = {(__bf16)(float)lane, (__bf16)1.0f, (__bf16)2.0f, (__bf16)3.0f,
+                    (__bf16)4.0f, (__bf16)5.0f, (__bf16)6.0f, (__bf16)7.0f};
+    const v8bf b = a;
+    v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) fsum += c0[v] + c1[v] + c2[v] + c3[v];
+  } else if constexpr (KIND == SVDQ_BENCH_MFMA_F32_32X32X1_2B) {
+    const float a = (float)lane, b = 1.0f + (float)lane;
+    typedef float v32f __attribute__((ext_vector_type(32)));
+    v32f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, c3, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 32; ++v) fsum += c0[v] + c1[v] + c2[v] + c3[v];
+  } else if constexpr (KIND == SVDQ_BENCH_VALU_FMA_F32) {
+    // 16 independent FMA chains per lane (one instruction each per round)
+    float f[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f[e] = (float)(lane + e);
+    const float m = 0.999f + 1e-9f * (float)lane, s = 1e-3f * (float)(lane + 1);  // registers, not literals
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) f[e] = __builtin_fmaf(f[e], m, s);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) fsum += f[e];
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    clk[2 * blockIdx.x] = t1 - t0;
+    clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
+  // keep the results live; the condition never holds for these inputs
+  if (isum == 0x7F3A5C19 || fsum == -1234.5f) sink[threadIdx.x] = isum + (int)fsum;
+}
+
+}  // namespace
+}  // namespace svdq
+
+extern "C" int svdq_bench_unit_peak(int kind, int blocks, int iters, unsigned long long* clocks, int* sink,
+                                    void* stream) {
+  if (clocks == nullptr || sink == nullptr) return -1;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 24)) return -2;
+  const dim3 grid(blocks), block(256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (kind) {
+    case SVDQ_BENCH_MFMA_I8_32X32X32:
+      hipLaunchKernelGGL(svdq::peak_kernel<SVDQ_BENCH_MFMA_I8_32X32X32>, grid, block, 0, st, iters, clocks, sink);
+      break;
+    case SVDQ_BENCH_MFMA_BF16_32X32X16:
+      hipLaunchKernelGGL(svdq::peak_kernel<SVDQ_BENCH_MFMA_BF16_32X32X16>, grid, block, 0, st, iters, clocks, sink);
+      break;
+    case SVDQ_BENCH_MFMA_F32_32X32X1_2B:
+      hipLaunchKernelGGL(svdq::peak_kernel<SVDQ_BENCH_MFMA_F32_32X32X1_2B>, grid, block, 0, st, iters, clocks, sink);
+      break;
+    case SVDQ_BENCH_VALU_FMA_F32:
+      hipLaunchKernelGGL(svdq::peak_kernel<SVDQ_BENCH_VALU_FMA_F32>, grid, block, 0, st, iters, clocks, sink);
+      break;
+    default:
+      return -4;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}

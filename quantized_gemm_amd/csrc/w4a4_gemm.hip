@@ -1,16 +1,35 @@
-// Kernel (b): the plain W4A4 layer (no activation) and the exact group-sum export, and the
-// dispatch of svdq_linear_w4a4* to the translation unit that holds each epilogue's kernels (each
-// unit instantiates the kernel for the 17 ranks; splitting them lets the build compile in parallel).
+// Kernel (b): dispatch of svdq_linear_w4a4* over the epilogue and the rank, and the exact
+// group-sum export. The kernel's instantiations for the 17 ranks and 3 epilogues are compiled in
+// separate units (build.py generates them from w4a4_gemm_kernel.h) so that the build runs them in
+// parallel; this unit only references them.
 #include "w4a4_gemm_kernel.h"
 
 namespace svdq {
 
+namespace {
+
+template <int EPI>
+hipError_t launch_epi(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                      const uint16_t* t, const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y, int M, int N,
+                      int K, const W4A4Epilogue& epi, hipStream_t stream) {
+#define SVDQ_CASE(NR) \
+  case NR: return launch_nr<NR, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+  switch (r / 16) {
+    SVDQ_CASE(0) SVDQ_CASE(1) SVDQ_CASE(2) SVDQ_CASE(3) SVDQ_CASE(4) SVDQ_CASE(5) SVDQ_CASE(6) SVDQ_CASE(7)
+    SVDQ_CASE(8) SVDQ_CASE(9) SVDQ_CASE(10) SVDQ_CASE(11) SVDQ_CASE(12) SVDQ_CASE(13) SVDQ_CASE(14)
+    SVDQ_CASE(15) SVDQ_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef SVDQ_CASE
+}
+
+}  // namespace
+
 hipError_t launch_w4a4_gemm(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                             const uint16_t* t, const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y,
                             int M, int N, int K, const W4A4Epilogue& epi, hipStream_t stream) {
-  if (epi.gelu) return launch_w4a4_gemm_gelu(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-  if (epi.qkv_heads > 0)
-    return launch_w4a4_gemm_qkv(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+  if (epi.gelu) return launch_epi<1>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
+  if (epi.qkv_heads > 0) return launch_epi<2>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
   return launch_epi<0>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
 }
 

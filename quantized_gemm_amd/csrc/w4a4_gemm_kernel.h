@@ -415,7 +415,17 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
   }
 }
 
-// Launch of the W4A4 layer with epilogue EPI for rank r = 16 * NR, and the dispatch over r.
+}  // namespace
+
+// Launch of the W4A4 layer with epilogue EPI for rank r = 16 * NR. Declared for every unit; the
+// definition (and with it the kernel's machine code) is compiled only in the units that define
+// SVDQ_W4A4_INSTANTIATE, each for a few ranks, so that the build compiles them in parallel.
+template <int NR, int EPI>
+hipError_t launch_nr(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw, const uint16_t* t,
+                     const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y, int M, int N, int K,
+                     const W4A4Epilogue& epi, hipStream_t stream);
+
+#ifdef SVDQ_W4A4_INSTANTIATE
 template <int NR, int EPI>
 hipError_t launch_nr(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw, const uint16_t* t,
                      const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y, int M, int N, int K,
@@ -427,32 +437,6 @@ hipError_t launch_nr(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
                      epi.rope_cos, epi.rope_sin, nullptr, 0, 0, 0, 0);
   return hipGetLastError();
 }
+#endif
 
-template <int EPI>
-hipError_t launch_epi(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
-                      const uint16_t* t, const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y, int M, int N,
-                      int K, const W4A4Epilogue& epi, hipStream_t stream) {
-  switch (r / 16) {
-    case 0: return launch_nr<0, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 1: return launch_nr<1, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 2: return launch_nr<2, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 3: return launch_nr<3, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 4: return launch_nr<4, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 5: return launch_nr<5, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 6: return launch_nr<6, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 7: return launch_nr<7, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 8: return launch_nr<8, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 9: return launch_nr<9, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 10: return launch_nr<10, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 11: return launch_nr<11, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 12: return launch_nr<12, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 13: return launch_nr<13, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 14: return launch_nr<14, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 15: return launch_nr<15, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    case 16: return launch_nr<16, EPI>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-}  // namespace
 }  // namespace svdq

@@ -28,12 +28,13 @@ def resources():
 
 def test_every_kernel_instantiation_reported(resources):
     count = lambda src: sum(1 for r in resources if r[0] == src)
-    # quantizer and GEMM: one instantiation per rank r = 16 q, q = 0..16 (+ the GEMM's debug dump);
-    # the GEMM's GELU and fused-QKV epilogues in their own units
+    # quantizer: one instantiation per rank r = 16 q, q = 0..16
     assert count("quant_act.hip") == 17
-    assert count("w4a4_gemm.hip") == 18
-    assert count("w4a4_gemm_gelu.hip") == 17
-    assert count("w4a4_gemm_qkv.hip") == 17
+    # GEMM: the debug dump in the dispatch unit, and the 17 ranks x 3 epilogues in the generated units
+    assert count("w4a4_gemm.hip") == 1
+    gemm = [r for r in resources if r[0].startswith("w4a4_inst_") and "w4a4_gemm_kernel" in r[1]]
+    assert len(gemm) == 17 * 3
+    assert len({r[1] for r in gemm}) == 17 * 3
     assert count("w4a16_gemv.hip") == 1
 
 
