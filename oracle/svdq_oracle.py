@@ -58,6 +58,8 @@ __all__ = [
     "quantize_weights_w4a4", "smooth_activations", "quantize_activations", "lowrank_down",
     "group_sums", "dequant_product", "svdq_linear", "svdq_layer", "quantize_weights_w4a16",
     "awq_linear", "gelu_tanh", "svdq_linear_gelu", "qkv_norm_rope",
+    "MX_BLOCK", "E2M1_VALUES", "e2m1_decode", "e2m1_round", "mxfp4_quantize_rows", "mxfp4_dequant",
+    "quantize_activations_mxfp4", "quantize_weights_mxfp4", "svdq_linear_mxfp4", "svdq_layer_mxfp4",
 ]
 
 
@@ -291,3 +293,113 @@ def awq_linear(x, codes, scales, bias=None):
     if bias is not None:
         y = y + bias.astype(np.float64)[None, :]
     return y, bf16_round(y.astype(np.float32))
+
+
+
+# ----------------------------------------------------------------------------------------------
+# The 4-bit float variant: MXFP4 (E2M1 elements, one E8M0 power-of-two scale per block of 32)
+# ----------------------------------------------------------------------------------------------
+# The pages name a 4-bit float precision for svdq_w4a4 layers beside INT4 (the Nunchaku README's
+# news and performance notes on NVFP4, the Diffusers blog's quantization_config with precision
+# "nvfp4" and group_size 16, the Z-Image guide's "INT4 vs NVFP4" table) but do not define the
+# format. Reading: on CDNA4 the matrix cores take the OCP Microscaling (MX) formats natively, so
+# the variant built here is MXFP4 as that specification defines it:
+#   * an element is FP4 E2M1: sign bit, 2 exponent bits (bias 1), 1 mantissa bit; the magnitudes
+#     are 0, 0.5 (exponent field 0: mantissa x 0.5), 1, 1.5, 2, 3, 4, 6 (2^(E-1) (1 + M/2));
+#     its 4-bit code is (S << 3) | (E << 1) | M;
+#   * each block of 32 consecutive values along K shares one E8M0 scale X = 2^e (byte e + 127),
+#     e = floor(log2(absmax)) - 2 (2 = the largest E2M1 exponent), clamped to [-127, 127];
+#     an all-zero block gets byte 0;
+#   * element = v / X rounded to the nearest E2M1 value, ties to the even mantissa, magnitudes
+#     above 6 saturate to 6; the sign bit is the sign bit of v.
+# The layer is otherwise unchanged: Y = X_hat L1 L2 + dequant(MXFP4(X_hat) MXFP4(R)) + b.
+
+MX_BLOCK = 32
+E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)   # magnitude of codes 0..7, by the definition
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """4-bit E2M1 codes -> float64 values, from the field definition (not a table lookup)."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(s == 1, -mag, mag)
+
+
+def e2m1_round(q) -> np.ndarray:
+    """Nearest E2M1 magnitude code (0..7) of |q| (float64), ties to the even code, saturating at 6:
+    every candidate's distance is compared, the closest wins, an exact tie goes to the code whose
+    mantissa bit (the lowest bit) is 0."""
+    a = np.abs(np.asarray(q, dtype=np.float64))
+    grid = np.array(E2M1_VALUES)
+    d = np.abs(a[..., None] - grid)                        # exact: a is a float, grid values are dyadic
+    best = np.argmin(d, axis=-1)                           # first (lowest) code among equal distances
+    dmin = np.take_along_axis(d, best[..., None], axis=-1)[..., 0]
+    nxt = np.minimum(best + 1, 7)
+    tie = (np.take_along_axis(d, nxt[..., None], axis=-1)[..., 0] == dmin) & (nxt != best)
+    code = np.where(tie & (best % 2 == 1), nxt, best)     # a tie between codes c, c+1: keep the even one
+    return np.where(a > 6.0, 7, code).astype(np.int64)
+
+
+def mxfp4_quantize_rows(v: np.ndarray):
+    """MXFP4 of each row of float32 ``v`` [rows, K], blocks of 32 consecutive entries.
+
+    Returns (codes uint8 [rows, K] holding 4-bit E2M1 codes, scales uint8 [rows, K/32] holding E8M0
+    bytes)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    rows, K = v.shape
+    assert K % MX_BLOCK == 0
+    vb = v.reshape(rows, K // MX_BLOCK, MX_BLOCK).astype(np.float64)
+    amax = np.max(np.abs(vb), axis=2)
+    _, ex = np.frexp(amax)                                 # amax = f 2^ex, f in [0.5, 1): floor(log2) = ex - 1
+    e = np.clip(ex - 1 - 2, -127, 127)
+    e = np.where(amax == 0, -127, e)
+    q = np.ldexp(vb, -e[:, :, None])                       # v / X, exact in float64
+    mag = e2m1_round(q)
+    sign = np.signbit(vb).astype(np.int64)
+    codes = (sign << 3) | mag
+    return codes.reshape(rows, K).astype(np.uint8), (e + 127).astype(np.uint8)
+
+
+def mxfp4_dequant(codes, scales) -> np.ndarray:
+    """float64 values of MXFP4 rows: codes uint8 [rows, K], scales uint8 [rows, K/32]."""
+    c = np.asarray(codes)
+    rows, K = c.shape
+    e = np.asarray(scales, dtype=np.int64) - 127
+    return e2m1_decode(c) * np.ldexp(1.0, np.repeat(e, MX_BLOCK, axis=1))
+
+
+def quantize_activations_mxfp4(x: np.ndarray, inv: np.ndarray, l1_bf16=None):
+    """The fused activation step of the MXFP4 layer: (codes uint8 [M, K], E8M0 scales uint8
+    [M, K/32], T or None); T exactly as in the INT4 layer."""
+    xh = smooth_activations(x, inv)
+    codes, sc = mxfp4_quantize_rows(xh)
+    t = None if l1_bf16 is None or l1_bf16.shape[1] == 0 else lowrank_down(xh, l1_bf16)
+    return codes, sc, t
+
+
+def quantize_weights_mxfp4(resid: np.ndarray):
+    """MXFP4 of the residual R [K, N] along K, per output column: (codes uint8 [N, K], scales
+    uint8 [N, K/32]) (one row per output column)."""
+    return mxfp4_quantize_rows(np.ascontiguousarray(resid.T))
+
+
+def svdq_linear_mxfp4(qa, sa, qw, sw, t=None, l2_bf16=None, bias=None):
+    """Y = dequant(MXFP4(X_hat)) dequant(MXFP4(R)) + T L2 + b in float64; returns (float64,
+    bf16-rounded float32). qa/sa per token, qw/sw per output column."""
+    y = mxfp4_dequant(qa, sa) @ mxfp4_dequant(qw, sw).T
+    if t is not None and l2_bf16 is not None and l2_bf16.shape[0] > 0:
+        y = y + t.astype(np.float64) @ l2_bf16.astype(np.float64)
+    if bias is not None:
+        y = y + bias.astype(np.float64)[None, :]
+    return y, bf16_round(y.astype(np.float32))
+
+
+def svdq_layer_mxfp4(x, inv, l1_bf16, l2_bf16, resid, bias=None):
+    """The MXFP4 layer from its prepared inputs; returns a dict of every intermediate."""
+    qa, sa, t = quantize_activations_mxfp4(x, inv, l1_bf16)
+    qw, sw = quantize_weights_mxfp4(resid)
+    y64, y = svdq_linear_mxfp4(qa, sa, qw, sw, t, l2_bf16, bias)
+    return {"qa": qa, "sa": sa, "t": t, "qw": qw, "sw": sw, "y64": y64, "y": y}
