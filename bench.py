@@ -79,6 +79,8 @@ def parse():
                          "rank sweep (r32/128/256), the W4A16 projection, and the unit peaks at the observed clock")
     ap.add_argument("--unit-peaks", action="store_true",
                     help="only the execution-unit microbenchmarks (int8/bf16/f32 matrix core, f32 vector FMA)")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="the MXFP4 variant of the layer (quantizer, GEMM, layer) beside the INT4 layer, on --config")
     ap.add_argument("--only", choices=["gemm", "quant", "awq"], default=None,
                     help="launch one kernel of the default workload --steps times back to back (for counter runs)")
     ap.add_argument("--gemm-samples", type=int, default=200,
@@ -367,6 +369,20 @@ def mlp_pair(args):
         run(up, bu, xs[s % R], h, "gelu_tanh")
         run(dn, bd, h, y)
 
+    ws = torch.empty(q.load_library().svdq_gelu_quant_workspace_bytes(M, F, dn["r"]), dtype=torch.uint8, device=dev)
+
+    def fused_quant(s):
+        # the up projection's epilogue runs the down layer's activation step: H is never stored
+        q.svdq_quantize_act(xs[s % R], up["inv"], up["l1t"], *bu, stream=sh)
+        q.svdq_linear_w4a4_gelu_quant(bu[0], bu[1], up["qw"], up["sw"], bu[2], up["l2t"], up["bias"], dn["inv"],
+                                      dn["l1t"], *bd, workspace=ws, stream=sh)
+        q.svdq_linear_w4a4(bd[0], bd[1], dn["qw"], dn["sw"], bd[2], dn["l2t"], dn["bias"], y, stream=sh)
+
+    def up_gelu_quant(s):
+        q.svdq_quantize_act(xs[s % R], up["inv"], up["l1t"], *bu, stream=sh)
+        q.svdq_linear_w4a4_gelu_quant(bu[0], bu[1], up["qw"], up["sw"], bu[2], up["l2t"], up["bias"], dn["inv"],
+                                      dn["l1t"], *bd, workspace=ws, stream=sh)
+
     def separate(s):
         run(up, bu, xs[s % R], h)
         run(dn, bd, torch.nn.functional.gelu(h, approximate="tanh"), y)
@@ -394,8 +410,9 @@ def mlp_pair(args):
 
     n = max(1, args.steps)
     res = {}
-    for name, fn in (("pair_gelu_fused_us", fused), ("pair_gelu_separate_us", separate),
-                     ("up_plain_us", up_plain), ("up_gelu_fused_us", up_gelu), ("gelu_pass_torch_us", gelu_pass)):
+    for name, fn in (("pair_gelu_quant_fused_us", fused_quant), ("pair_gelu_fused_us", fused),
+                     ("pair_gelu_separate_us", separate), ("up_plain_us", up_plain), ("up_gelu_fused_us", up_gelu),
+                     ("up_gelu_quant_fused_us", up_gelu_quant), ("gelu_pass_torch_us", gelu_pass)):
         log(f"[mlp pair] {name}")
         res[name] = round(timed(fn, n), 2)
     ops = 2.0 * M * F * D * 2 + 2.0 * M * cu.rank * (D + F) + 2.0 * M * cd.rank * (F + D)
@@ -407,6 +424,8 @@ def mlp_pair(args):
                    "rotating_buffer_sets": R},
         **res,
         "pair_TOPS_fused": round(ops / (res["pair_gelu_fused_us"] * 1e-6) / 1e12, 1),
+        "pair_TOPS_gelu_quant_fused": round(ops / (res["pair_gelu_quant_fused_us"] * 1e-6) / 1e12, 1),
+        "saved_by_quant_fusion_us": round(res["pair_gelu_fused_us"] - res["pair_gelu_quant_fused_us"], 2),
         "gelu_epilogue_cost_us": round(res["up_gelu_fused_us"] - res["up_plain_us"], 2),
         "saved_by_fusion_us": round(res["pair_gelu_separate_us"] - res["pair_gelu_fused_us"], 2),
     }
@@ -747,6 +766,95 @@ def all_configs(args):
     print(json.dumps(out), flush=True)
 
 
+FP4_PEAK_TOPS = 10066.3    # 256 CU x 2.4 GHz x 16384 FP4 ops / clk / CU (published 10.1 PFLOP/s dense)
+
+
+def mxfp4_bench(args):
+    """The 4-bit float (MXFP4) variant of the layer on one configuration (default: the MLP up
+    projection): the quantizer, the GEMM (block scales applied inside the scaled FP4 matrix
+    instruction) and the layer, each back to back over rotating buffer sets, beside the INT4 layer
+    on the same problem. The GEMM is reported against the FP4 and the int8 dense peaks."""
+    import torch
+    import synth
+    import quantized_gemm_amd as q
+    from quantized_gemm_amd import prep
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    q.load_library()
+    q.svdq_check_device()
+    cfg = synth.CONFIGS[args.config]
+    M, K, N, r = cfg.M, cfg.K, cfg.N, cfg.rank
+    log(f"[mxfp4] {cfg.name} M={M} K={K} N={N} r={r}: preparing")
+    inp = synth.make_layer_inputs(cfg)
+    d = prep.decompose(synth.f32_from_bf16_bits(inp["x"]), synth.f32_from_bf16_bits(inp["w"]), r)
+    qwm, swm = q.svdq_pack_weights(q.SVDQ_FMT_MXFP4_E8M0SCALE, d["resid"])
+    qwi, swi = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, d["resid"])
+    l1t, l2t = q.svdq_pack_lowrank(d["l1"], d["l2"])
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    R = int(min(16, max(4, -(-600_000_000 // quant_bytes(M, K, r)))))
+    xs = [bf16_dev(inp["x"]) for _ in range(R)]
+    inv = torch.from_numpy(d["inv_smooth"]).to(dev)
+    qwm_d, swm_d = torch.from_numpy(qwm).to(dev), torch.from_numpy(swm).to(dev)
+    qwi_d, swi_d = torch.from_numpy(qwi).to(dev), torch.from_numpy(swi).to(dev)
+    l1t_d, l2t_d, bias_d = bf16_dev(l1t), bf16_dev(l2t), bf16_dev(inp["bias"])
+    qa = [torch.empty((K // 64, M, 32), dtype=torch.uint8, device=dev) for _ in range(R)]
+    sam = [torch.empty((K // 64, M, 2), dtype=torch.uint8, device=dev) for _ in range(R)]
+    sai = [torch.empty((K // 64, M), dtype=torch.float32, device=dev) for _ in range(R)]
+    tl = [torch.empty((M, r), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def quant_mx(s):
+        k = s % R
+        q.svdq_quantize_act_mxfp4(xs[k], inv, l1t_d, qa[k], sam[k], tl[k], stream=sh)
+
+    def gemm_mx(s):
+        k = s % R
+        q.svdq_linear_mxfp4(qa[k], sam[k], qwm_d, swm_d, tl[k], l2t_d, bias_d, y, stream=sh)
+
+    def quant_i4(s):
+        k = s % R
+        q.svdq_quantize_act(xs[k], inv, l1t_d, qa[k], sai[k], tl[k], stream=sh)
+
+    def gemm_i4(s):
+        k = s % R
+        q.svdq_linear_w4a4(qa[k], sai[k], qwi_d, swi_d, tl[k], l2t_d, bias_d, y, stream=sh)
+
+    n = max(20, args.steps)
+    for s in range(R):
+        quant_mx(s)
+    torch.cuda.synchronize()
+    log("[mxfp4] timing")
+    tq, tg = batch_timing(quant_mx, stream, n), batch_timing(gemm_mx, stream, n)
+    tl_mx = batch_timing(lambda s: (quant_mx(s), gemm_mx(s)), stream, n)
+    for s in range(R):
+        quant_i4(s)
+    torch.cuda.synchronize()
+    tqi, tgi = batch_timing(quant_i4, stream, n), batch_timing(gemm_i4, stream, n)
+    tli = batch_timing(lambda s: (quant_i4(s), gemm_i4(s)), stream, n)
+    ops = 2.0 * M * N * K
+    lr = 2.0 * M * r * (K + N)
+    mx_tops = ops / (tg["median"] * 1e-6) / 1e12
+    out = {
+        "metric": f"MXFP4 variant of the layer ({cfg.name} M{M} K{K} N{N} r{r})",
+        "unit": "us", "steps": n, "rotating_buffer_sets": R,
+        "mxfp4": {"quantize_act_us": tq, "linear_us": tg, "layer_us": tl_mx,
+                  "linear_TOPS": round(mx_tops, 1), "frac_fp4_peak": round(mx_tops / FP4_PEAK_TOPS, 4),
+                  "frac_int8_peak": round(mx_tops / INT8_PEAK_TOPS, 4),
+                  "layer_TOPS": round((ops + lr) / (tl_mx["median"] * 1e-6) / 1e12, 1)},
+        "int4": {"quantize_act_us": tqi, "linear_us": tgi, "layer_us": tli,
+                 "linear_TOPS": round(ops / (tgi["median"] * 1e-6) / 1e12, 1),
+                 "layer_TOPS": round((ops + lr) / (tli["median"] * 1e-6) / 1e12, 1)},
+        "peaks_TOPS": {"fp4_dense": FP4_PEAK_TOPS, "int8_dense": INT8_PEAK_TOPS},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -768,6 +876,9 @@ def main():
         return
     if args.all_configs:
         all_configs(args)
+        return
+    if args.mxfp4:
+        mxfp4_bench(args)
         return
     if args.unit_peaks:
         import torch

@@ -97,7 +97,8 @@ enum svdq_status {
 
 enum svdq_format {
   SVDQ_FMT_W4A4_F32SCALE = 0,   /* residual weights for svdq_linear_w4a4, float32 scales */
-  SVDQ_FMT_W4A16_BF16SCALE = 1  /* weights for awq_linear_w4a16, bf16 scales */
+  SVDQ_FMT_W4A16_BF16SCALE = 1, /* weights for awq_linear_w4a16, bf16 scales */
+  SVDQ_FMT_MXFP4_E8M0SCALE = 2  /* residual weights for svdq_linear_mxfp4: E2M1 codes, E8M0 block-32 scales */
 };
 
 /* Name of a status code (static storage; never NULL). */
@@ -117,8 +118,8 @@ int svdq_check_device(void);
 /* Bytes of packed codes for a K x N weight: K*N/2 for either format; 0 if the shape is invalid. */
 size_t svdq_packed_weight_bytes(int fmt, int64_t K, int64_t N);
 
-/* Bytes of scales: (K/64)*N*4 for SVDQ_FMT_W4A4_F32SCALE, (K/64)*N*2 for SVDQ_FMT_W4A16_BF16SCALE;
- * 0 if the shape or format is invalid. */
+/* Bytes of scales: (K/64)*N*4 for SVDQ_FMT_W4A4_F32SCALE, (K/64)*N*2 for SVDQ_FMT_W4A16_BF16SCALE,
+ * (K/32)*N for SVDQ_FMT_MXFP4_E8M0SCALE; 0 if the shape or format is invalid. */
 size_t svdq_scale_bytes(int fmt, int64_t K, int64_t N);
 
 /* Quantize a float32 weight w [K, N] (row-major, x @ w convention) to INT4 with the rule above,
@@ -129,6 +130,10 @@ size_t svdq_scale_bytes(int fmt, int64_t K, int64_t N);
  *     qweight_out in the W4A16 block layout, scales_out bf16 [K/64, N].
  * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE (K % 64, N % 16), SVDQ_ERR_FORMAT. */
 int svdq_pack_weights(int fmt, const float* w, int64_t K, int64_t N, uint8_t* qweight_out, void* scales_out);
+
+/* (SVDQ_FMT_MXFP4_E8M0SCALE: w is the residual R; qweight_out K*N/2 bytes of E2M1 codes in the
+ * group-major W4A4 record layout; scales_out (K/32)*N E8M0 bytes [K/64, N, 2] -- see the MXFP4 entry
+ * points below for the rule.) */
 
 /* Round the low-rank factors to bf16 and transpose them into the kernels' operand order:
  * l1 float32 [K, r] -> l1t_out (r*K bf16, the L1t block order above); l2 float32 [r, N] ->
@@ -186,6 +191,61 @@ int svdq_linear_w4a4_qkv(const uint8_t* qact, const float* ascale, const uint8_t
                          const void* lora_act, const void* l2t, int r, const void* bias, void* y,
                          int64_t M, int64_t N, int64_t K, int heads, const float* q_norm_w, const float* k_norm_w,
                          const float* rope_cos, const float* rope_sin, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * The 4-bit float variant (MXFP4).
+ *
+ * The pages name a 4-bit float precision for svdq_w4a4 layers beside INT4 (the Nunchaku README's
+ * NVFP4 notes, the Diffusers blog's quantization_config with precision "nvfp4" and group_size 16,
+ * the Z-Image guide's "INT4 vs NVFP4" table) without defining the format. Reading: on CDNA4 the
+ * matrix cores take the OCP microscaling formats, so the variant is MXFP4: E2M1 elements (sign,
+ * 2-bit exponent with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; code
+ * (S << 3) | (E << 1) | M) and one E8M0 scale X = 2^e per block of 32 consecutive values along K,
+ * e = floor(log2(absmax)) - 2 clamped to [-127, 127], byte e + 127 (an all-zero block: byte 0);
+ * element = x / X rounded to the nearest E2M1 magnitude, ties to the even code, saturating at 6,
+ * with the sign bit of x. The layer is otherwise the INT4 layer: Y = X_hat L1 L2 + the product of
+ * the dequantized MXFP4 activations and residual + b.
+ *   Codes     K*rows/2 bytes in the INT4 group-major record: the 32 bytes of (slab g of 64, row)
+ *             at (g*rows + row)*32, byte b = codes of k = 64g + 2b (bits 0-3) and 64g + 2b + 1
+ *             (bits 4-7).
+ *   Scales    (K/32)*rows E8M0 bytes [K/64, rows, 2]: block 2g + h of a row at (g*rows + row)*2 + h.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Fused activation step of the MXFP4 layer: as svdq_quantize_act, with MXFP4 codes (qact, K*M/2 bytes)
+ * and E8M0 scales (ascale, (K/32)*M bytes) in place of the INT4 codes and float32 scales. T is the same.
+ * Errors: as svdq_quantize_act. */
+int svdq_quantize_act_mxfp4(const void* x, int64_t M, int64_t K, const float* inv_smooth, const void* l1t, int r,
+                            uint8_t* qact, uint8_t* ascale, void* lora_act, void* stream);
+
+/* The MXFP4 product + up projection:
+ *   Y = bf16( sum_k dq(qact)[m,k] * dq(qweight)[k,n]  +  T L2  +  b ),  dq(c) = E2M1(c) * 2^(byte - 127)
+ * with float32 accumulation on the gfx950 scaled FP4 matrix instruction (the block scales are applied
+ * inside it). qweight / wscale from svdq_pack_weights(SVDQ_FMT_MXFP4_E8M0SCALE, R). Other arguments,
+ * layouts and errors as svdq_linear_w4a4. */
+int svdq_linear_mxfp4(const uint8_t* qact, const uint8_t* ascale, const uint8_t* qweight, const uint8_t* wscale,
+                      const void* lora_act, const void* l2t, int r, const void* bias, void* y,
+                      int64_t M, int64_t N, int64_t K, void* stream);
+
+/* The MLP pair fused across its boundary (the GELU/MLP execution path of the Diffusers blog on
+ * Nunchaku Lite, "From SVDQuant to Nunchaku Lite"): the up projection with the GELU of
+ * svdq_linear_w4a4_gelu, whose bf16 output H [M, N] is not stored; in its place the epilogue runs the
+ * next (down) layer's activation step on H exactly as svdq_quantize_act(H, inv_next, l1t_next, r_next)
+ * would: INT4 codes qact_next (N*M/2 bytes, group-major over the next layer's K = N), float32 scales
+ * ascale_next [N/64, M] and, when r_next > 0, T_next = bf16(bf16(H * inv_next) L1_next) (lora_act_next
+ * bf16 [M, r_next]). A group of 64 of the next layer lies inside one 128-column output tile, so codes
+ * and scales are tile-local; T_next sums over all N columns: each tile writes its float32 partial to
+ * the workspace and a second kernel adds the ceil(N/128) partials in tile order (deterministic).
+ *   workspace: device memory of svdq_gelu_quant_workspace_bytes(M, N, r_next) bytes (may be NULL when
+ *   r_next == 0), owned by the caller, overwritten; N % 64 == 0 is required.
+ * Up-layer arguments as svdq_linear_w4a4 (no y); next-layer arguments as svdq_quantize_act.
+ * Errors: those of svdq_linear_w4a4 and svdq_quantize_act; SVDQ_ERR_NULL for a missing or too small
+ * workspace; SVDQ_ERR_SHAPE if N % 64 != 0. */
+size_t svdq_gelu_quant_workspace_bytes(int64_t M, int64_t N, int r_next);
+int svdq_linear_w4a4_gelu_quant(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                                const void* lora_act, const void* l2t, int r, const void* bias, int64_t M, int64_t N,
+                                int64_t K, const float* inv_next, const void* l1t_next, int r_next, uint8_t* qact_next,
+                                float* ascale_next, void* lora_act_next, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* W4A16 projection (awq_w4a16 layers of the Diffusers blog): Y = bf16( X dequant(qweight, scales) + b ),
  * X bf16 [M, K], packed weights in the W4A16 block layout, scales bf16 [K/64, N], bias bf16 [N] or NULL.

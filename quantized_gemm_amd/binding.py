@@ -20,6 +20,7 @@ _lib = None
 SVDQ_OK = 0
 SVDQ_FMT_W4A4_F32SCALE = 0
 SVDQ_FMT_W4A16_BF16SCALE = 1
+SVDQ_FMT_MXFP4_E8M0SCALE = 2
 GROUP = 64
 
 _vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -40,6 +41,11 @@ _SIGNATURES = {
     "awq_linear_w4a16": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "svdq_debug_group_sums": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp]),
     "svdq_bench_unit_peak": (_int, [_int, _int, _int, _vp, _vp, _vp]),
+    "svdq_gelu_quant_workspace_bytes": (_sz, [_i64, _i64, _int]),
+    "svdq_linear_w4a4_gelu_quant": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _vp, _vp, _int,
+                                           _vp, _vp, _vp, _vp, _sz, _vp]),
+    "svdq_quantize_act_mxfp4": (_int, [_vp, _i64, _i64, _vp, _vp, _int, _vp, _vp, _vp, _vp]),
+    "svdq_linear_mxfp4": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
 
 
@@ -109,8 +115,11 @@ def svdq_pack_weights(fmt: int, w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     if qbytes == 0 or sbytes == 0:
         _check("svdq_pack_weights", lib.svdq_pack_weights(fmt, None, K, N, None, None) or -2)
     q = _aligned_empty(qbytes, np.uint8)
-    s = _aligned_empty(sbytes, np.float32 if fmt == SVDQ_FMT_W4A4_F32SCALE else np.uint16)
+    sdt = {SVDQ_FMT_W4A4_F32SCALE: np.float32, SVDQ_FMT_W4A16_BF16SCALE: np.uint16}.get(fmt, np.uint8)
+    s = _aligned_empty(sbytes, sdt)
     _check("svdq_pack_weights", lib.svdq_pack_weights(fmt, _np_ptr(w), K, N, _np_ptr(q), _np_ptr(s)))
+    if fmt == SVDQ_FMT_MXFP4_E8M0SCALE:
+        return q, s.reshape(K // GROUP, N, 2)
     return q, s.reshape(K // GROUP, N)
 
 
@@ -295,3 +304,93 @@ def svdq_bench_unit_peak(kind: str, blocks: int, iters: int, clocks, sink, strea
                                              _dev_ptr(sink, "sink", (torch.int32,), (256,)), _stream(stream))
     if st != 0:
         raise RuntimeError(f"svdq_bench_unit_peak failed with {st}")
+
+
+def svdq_quantize_act_mxfp4(x, inv_smooth, l1t, qact=None, ascale=None, lora_act=None, stream=None):
+    """Kernel (a) of the MXFP4 variant. Returns (qact uint8 [K/64, M, 32] E2M1 codes, ascale uint8
+    [K/64, M, 2] E8M0 bytes, lora_act bf16 [M, r] or None)."""
+    import torch
+    M, K = x.shape
+    r = 0 if l1t is None else l1t.shape[0]
+    dev = x.device
+    if qact is None:
+        qact = torch.empty((K // GROUP, M, 32), dtype=torch.uint8, device=dev)
+    if ascale is None:
+        ascale = torch.empty((K // GROUP, M, 2), dtype=torch.uint8, device=dev)
+    if r and lora_act is None:
+        lora_act = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+    st = load_library().svdq_quantize_act_mxfp4(
+        _dev_ptr(x, "x", _bf16()), M, K, _dev_ptr(inv_smooth, "inv_smooth", (torch.float32,), (K,)),
+        _dev_ptr(l1t, "l1t", _bf16(), (r, K) if r else None), r,
+        _dev_ptr(qact, "qact", (torch.uint8,), (K // GROUP, M, 32)),
+        _dev_ptr(ascale, "ascale", (torch.uint8,), (K // GROUP, M, 2)),
+        _dev_ptr(lora_act, "lora_act", _bf16(), (M, r)) if r else None, _stream(stream))
+    _check("svdq_quantize_act_mxfp4", st)
+    return qact, ascale, (lora_act if r else None)
+
+
+def svdq_linear_mxfp4(qact, ascale, qweight, wscale, lora_act, l2t, bias, y=None, stream=None):
+    """Kernel (b) of the MXFP4 variant. qact uint8 [K/64, M, 32], ascale uint8 [K/64, M, 2],
+    qweight uint8 (K*N/2 bytes), wscale uint8 [K/64, N, 2]. Returns y bf16 [M, N]."""
+    import torch
+    G, M, _ = ascale.shape
+    K = G * GROUP
+    N = wscale.shape[1]
+    if qact.numel() != M * K // 2:
+        raise ValueError("qact size does not match K*M/2")
+    if qweight.numel() != N * K // 2:
+        raise ValueError("qweight size does not match [N, K/2]")
+    r = 0 if l2t is None else l2t.shape[1]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=qact.device)
+    u8 = (torch.uint8,)
+    st = load_library().svdq_linear_mxfp4(
+        _dev_ptr(qact, "qact", u8), _dev_ptr(ascale, "ascale", u8, (G, M, 2)), _dev_ptr(qweight, "qweight", u8),
+        _dev_ptr(wscale, "wscale", u8, (G, N, 2)), _dev_ptr(lora_act, "lora_act", _bf16(), (M, r)) if r else None,
+        _dev_ptr(l2t, "l2t", _bf16(), (N, r)) if r else None, r, _dev_ptr(bias, "bias", _bf16(), (N,)),
+        _dev_ptr(y, "y", _bf16(), (M, N)), M, N, K, _stream(stream))
+    _check("svdq_linear_mxfp4", st)
+    return y
+
+
+def svdq_linear_w4a4_gelu_quant(qact, ascale, qweight, wscale, lora_act, l2t, bias, inv_next, l1t_next, qact_next=None,
+                                ascale_next=None, lora_act_next=None, workspace=None, stream=None):
+    """The MLP up projection with its GELU and the next layer's activation step fused into the
+    epilogue (H is not stored). Returns (qact_next uint8 [N/64, M, 32], ascale_next float32 [N/64, M],
+    lora_act_next bf16 [M, r_next] or None)."""
+    import torch
+    G, M = ascale.shape
+    K = G * GROUP
+    N = wscale.shape[1]
+    if qact.numel() != M * K // 2:
+        raise ValueError("qact size does not match K*M/2")
+    if qweight.numel() != N * K // 2:
+        raise ValueError("qweight size does not match [N, K/2]")
+    r = 0 if l2t is None else l2t.shape[1]
+    rn = 0 if l1t_next is None else l1t_next.shape[0]
+    dev = qact.device
+    lib = load_library()
+    if qact_next is None:
+        qact_next = torch.empty((N // GROUP, M, 32), dtype=torch.uint8, device=dev)
+    if ascale_next is None:
+        ascale_next = torch.empty((N // GROUP, M), dtype=torch.float32, device=dev)
+    if rn and lora_act_next is None:
+        lora_act_next = torch.empty((M, rn), dtype=torch.bfloat16, device=dev)
+    need = lib.svdq_gelu_quant_workspace_bytes(M, N, rn)
+    if rn and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    f32 = (torch.float32,)
+    st = lib.svdq_linear_w4a4_gelu_quant(
+        _dev_ptr(qact, "qact", (torch.uint8,)), _dev_ptr(ascale, "ascale", f32, (G, M)),
+        _dev_ptr(qweight, "qweight", (torch.uint8,)), _dev_ptr(wscale, "wscale", f32, (G, N)),
+        _dev_ptr(lora_act, "lora_act", _bf16(), (M, r)) if r else None,
+        _dev_ptr(l2t, "l2t", _bf16(), (N, r)) if r else None, r, _dev_ptr(bias, "bias", _bf16(), (N,)), M, N, K,
+        _dev_ptr(inv_next, "inv_next", f32, (N,)), _dev_ptr(l1t_next, "l1t_next", _bf16(), (rn, N)) if rn else None,
+        rn, _dev_ptr(qact_next, "qact_next", (torch.uint8,), (N // GROUP, M, 32)),
+        _dev_ptr(ascale_next, "ascale_next", f32, (N // GROUP, M)),
+        _dev_ptr(lora_act_next, "lora_act_next", _bf16(), (M, rn)) if rn else None,
+        _dev_ptr(workspace, "workspace", (torch.uint8,)) if rn else None,
+        int(workspace.numel()) if rn else 0, _stream(stream))
+    _check("svdq_linear_w4a4_gelu_quant", st)
+    return qact_next, ascale_next, (lora_act_next if rn else None)
+

@@ -138,6 +138,88 @@ int svdq_linear_w4a4_qkv(const uint8_t* qact, const float* ascale, const uint8_t
   return linear_w4a4(qact, ascale, qweight, wscale, lora_act, l2t, r, bias, y, M, N, K, epi, stream);
 }
 
+size_t svdq_gelu_quant_workspace_bytes(int64_t M, int64_t N, int r_next) {
+  if (!mk_ok(M, 64) || !n_ok(N) || N % SVDQ_GROUP != 0 || !rank_ok(r_next)) return 0;
+  return static_cast<size_t>(((N + 127) / 128) * M * r_next * 4);
+}
+
+int svdq_linear_w4a4_gelu_quant(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
+                                const void* lora_act, const void* l2t, int r, const void* bias, int64_t M, int64_t N,
+                                int64_t K, const float* inv_next, const void* l1t_next, int r_next, uint8_t* qact_next,
+                                float* ascale_next, void* lora_act_next, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (qact == nullptr || ascale == nullptr || qweight == nullptr || wscale == nullptr || inv_next == nullptr ||
+      qact_next == nullptr || ascale_next == nullptr)
+    return SVDQ_ERR_NULL;
+  if (!aligned16(qact) || !aligned16(ascale) || !aligned16(qweight) || !aligned16(wscale) ||
+      (lora_act && !aligned16(lora_act)) || (l2t && !aligned16(l2t)) || (bias && !aligned16(bias)) ||
+      !aligned16(inv_next) || (l1t_next && !aligned16(l1t_next)) || !aligned16(qact_next) ||
+      !aligned16(ascale_next) || (lora_act_next && !aligned16(lora_act_next)) || (workspace && !aligned16(workspace)))
+    return SVDQ_ERR_NULL;
+  if (!mk_ok(M, K) || !n_ok(N) || N % SVDQ_GROUP != 0 || N * K >= (int64_t(1) << 40) || M * N >= (int64_t(1) << 40))
+    return SVDQ_ERR_SHAPE;
+  if (!rank_ok(r) || !rank_ok(r_next)) return SVDQ_ERR_RANK;
+  if ((r == 0) != (lora_act == nullptr) || (r == 0) != (l2t == nullptr)) return SVDQ_ERR_RANK;
+  if ((r_next == 0) != (l1t_next == nullptr) || (r_next == 0) != (lora_act_next == nullptr)) return SVDQ_ERR_RANK;
+  const size_t need = svdq_gelu_quant_workspace_bytes(M, N, r_next);
+  if (r_next > 0 && (workspace == nullptr || workspace_bytes < need)) return SVDQ_ERR_NULL;
+  const int st = device_status();
+  if (st != SVDQ_OK) return st;
+  svdq::W4A4Epilogue epi;
+  epi.quant_next = true;
+  epi.next.inv = inv_next;
+  epi.next.l1t = static_cast<const uint16_t*>(l1t_next);
+  epi.next.r = r_next;
+  epi.next.qact = qact_next;
+  epi.next.ascale = ascale_next;
+  epi.next.tpart = static_cast<float*>(workspace);
+  hipStream_t sh = static_cast<hipStream_t>(stream);
+  const int rs = launch_status(svdq::launch_w4a4_gemm(qact, ascale, qweight, wscale,
+                                                      static_cast<const uint16_t*>(lora_act),
+                                                      static_cast<const uint16_t*>(l2t), r,
+                                                      static_cast<const uint16_t*>(bias), nullptr, (int)M, (int)N,
+                                                      (int)K, epi, sh));
+  if (rs != SVDQ_OK || r_next == 0) return rs;
+  return launch_status(svdq::launch_tpart_reduce(static_cast<const float*>(workspace), (int)((N + 127) / 128), (int)M,
+                                                 r_next, static_cast<uint16_t*>(lora_act_next), sh));
+}
+
+int svdq_quantize_act_mxfp4(const void* x, int64_t M, int64_t K, const float* inv_smooth, const void* l1t, int r,
+                            uint8_t* qact, uint8_t* ascale, void* lora_act, void* stream) {
+  if (x == nullptr || qact == nullptr || ascale == nullptr) return SVDQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(qact) || !aligned16(ascale) || (inv_smooth && !aligned16(inv_smooth)) ||
+      (l1t && !aligned16(l1t)) || (lora_act && !aligned16(lora_act)))
+    return SVDQ_ERR_NULL;
+  if (!mk_ok(M, K)) return SVDQ_ERR_SHAPE;
+  if (!rank_ok(r)) return SVDQ_ERR_RANK;
+  if ((r == 0) != (l1t == nullptr) || (r == 0) != (lora_act == nullptr)) return SVDQ_ERR_RANK;
+  const int st = device_status();
+  if (st != SVDQ_OK) return st;
+  return launch_status(svdq::launch_quantize_act_mxfp4(static_cast<const uint16_t*>(x), (int)M, (int)K, inv_smooth,
+                                                       static_cast<const uint16_t*>(l1t), r, qact, ascale,
+                                                       static_cast<uint16_t*>(lora_act),
+                                                       static_cast<hipStream_t>(stream)));
+}
+
+int svdq_linear_mxfp4(const uint8_t* qact, const uint8_t* ascale, const uint8_t* qweight, const uint8_t* wscale,
+                      const void* lora_act, const void* l2t, int r, const void* bias, void* y, int64_t M, int64_t N,
+                      int64_t K, void* stream) {
+  if (qact == nullptr || ascale == nullptr || qweight == nullptr || wscale == nullptr || y == nullptr)
+    return SVDQ_ERR_NULL;
+  if (!aligned16(qact) || !aligned16(ascale) || !aligned16(qweight) || !aligned16(wscale) || !aligned16(y) ||
+      (lora_act && !aligned16(lora_act)) || (l2t && !aligned16(l2t)) || (bias && !aligned16(bias)))
+    return SVDQ_ERR_NULL;
+  if (!mk_ok(M, K) || !n_ok(N) || N * K >= (int64_t(1) << 40) || M * N >= (int64_t(1) << 40)) return SVDQ_ERR_SHAPE;
+  if (!rank_ok(r)) return SVDQ_ERR_RANK;
+  if ((r == 0) != (lora_act == nullptr) || (r == 0) != (l2t == nullptr)) return SVDQ_ERR_RANK;
+  const int st = device_status();
+  if (st != SVDQ_OK) return st;
+  return launch_status(svdq::launch_mxfp4_gemm(qact, ascale, qweight, wscale, static_cast<const uint16_t*>(lora_act),
+                                               static_cast<const uint16_t*>(l2t), r,
+                                               static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), (int)M,
+                                               (int)N, (int)K, static_cast<hipStream_t>(stream)));
+}
+
 int awq_linear_w4a16(const void* x, const uint8_t* qweight, const void* scales, const void* bias, void* y, int64_t M,
                      int64_t N, int64_t K, void* stream) {
   if (x == nullptr || qweight == nullptr || scales == nullptr || y == nullptr) return SVDQ_ERR_NULL;

@@ -133,12 +133,54 @@ void pack_w4a16(const float* w, int64_t K, int64_t N, uint8_t* q, uint16_t* scal
   }
 }
 
+// MXFP4 (the 4-bit float variant): one E8M0 byte per (column, block of 32 along K), byte =
+// floor(log2 amax) - 2 + 127 clamped to [0, 254] (0 for an all-zero block); element = the E2M1 code of
+// w / 2^(byte - 127) rounded to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 (ties to the even code,
+// saturating at 6), sign bit from w.
+inline uint32_t mx_byte(float amax) {
+  uint32_t u;
+  std::memcpy(&u, &amax, 4);
+  const uint32_t be = u >> 23;            // amax >= 0: the biased exponent (0 for zero / subnormal)
+  return be < 2 ? 0u : be - 2u;
+}
+
+inline uint32_t e2m1(float v, uint32_t byte) {
+  const double a = std::fabs(std::ldexp(static_cast<double>(v), 127 - static_cast<int>(byte)));  // exact
+  const uint32_t mag = (a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0);
+  return (std::signbit(v) ? 8u : 0u) | mag;
+}
+
+void pack_mxfp4(const float* w, int64_t K, int64_t N, uint8_t* q, uint8_t* scales) {
+  const int64_t B = K / 32;  // blocks of 32 along K
+  std::vector<float> amax(static_cast<size_t>(B * N), 0.0f);
+  for (int64_t k = 0; k < K; ++k) {
+    float* am = amax.data() + (k / 32) * N;
+    const float* row = w + k * N;
+    for (int64_t n = 0; n < N; ++n) am[n] = std::fmax(am[n], std::fabs(row[n]));
+  }
+  // scales [K/64, N, 2]: block b = 2g + h of column n at (g*N + n)*2 + h
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t n = 0; n < N; ++n)
+      scales[((b / 2) * N + n) * 2 + (b % 2)] = static_cast<uint8_t>(mx_byte(amax[static_cast<size_t>(b * N + n)]));
+  std::memset(q, 0, static_cast<size_t>(K * N / 2));
+  for (int64_t k = 0; k < K; ++k) {
+    const int64_t g = k / SVDQ_GROUP, b = k / 32;
+    const float* row = w + k * N;
+    const int shift = (k & 1) ? 4 : 0;
+    uint8_t* qg = q + g * N * 32 + (k % SVDQ_GROUP) / 2;
+    for (int64_t n = 0; n < N; ++n) {
+      const uint32_t byte = scales[(g * N + n) * 2 + (b % 2)];
+      qg[n * 32] |= static_cast<uint8_t>(e2m1(row[n], byte) << shift);
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t svdq_packed_weight_bytes(int fmt, int64_t K, int64_t N) {
-  if (fmt != SVDQ_FMT_W4A4_F32SCALE && fmt != SVDQ_FMT_W4A16_BF16SCALE) return 0;
+  if (fmt != SVDQ_FMT_W4A4_F32SCALE && fmt != SVDQ_FMT_W4A16_BF16SCALE && fmt != SVDQ_FMT_MXFP4_E8M0SCALE) return 0;
   if (!shape_ok(K, N)) return 0;
   return static_cast<size_t>(K * N / 2);
 }
@@ -147,18 +189,22 @@ size_t svdq_scale_bytes(int fmt, int64_t K, int64_t N) {
   if (!shape_ok(K, N)) return 0;
   if (fmt == SVDQ_FMT_W4A4_F32SCALE) return static_cast<size_t>((K / SVDQ_GROUP) * N * 4);
   if (fmt == SVDQ_FMT_W4A16_BF16SCALE) return static_cast<size_t>((K / SVDQ_GROUP) * N * 2);
+  if (fmt == SVDQ_FMT_MXFP4_E8M0SCALE) return static_cast<size_t>((K / 32) * N);
   return 0;
 }
 
 int svdq_pack_weights(int fmt, const float* w, int64_t K, int64_t N, uint8_t* qweight_out, void* scales_out) {
-  if (fmt != SVDQ_FMT_W4A4_F32SCALE && fmt != SVDQ_FMT_W4A16_BF16SCALE) return SVDQ_ERR_FORMAT;
+  if (fmt != SVDQ_FMT_W4A4_F32SCALE && fmt != SVDQ_FMT_W4A16_BF16SCALE && fmt != SVDQ_FMT_MXFP4_E8M0SCALE)
+    return SVDQ_ERR_FORMAT;
   if (w == nullptr || qweight_out == nullptr || scales_out == nullptr) return SVDQ_ERR_NULL;
   if (!shape_ok(K, N)) return SVDQ_ERR_SHAPE;
   IeeeDenormalGuard guard;
   if (fmt == SVDQ_FMT_W4A4_F32SCALE)
     pack_w4a4(w, K, N, qweight_out, static_cast<float*>(scales_out));
-  else
+  else if (fmt == SVDQ_FMT_W4A16_BF16SCALE)
     pack_w4a16(w, K, N, qweight_out, static_cast<uint16_t*>(scales_out));
+  else
+    pack_mxfp4(w, K, N, qweight_out, static_cast<uint8_t*>(scales_out));
   return SVDQ_OK;
 }
 

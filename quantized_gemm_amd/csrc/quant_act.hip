@@ -24,6 +24,7 @@
 // for the rare undecided group.
 #include <float.h>
 
+#include "quant_rules.h"
 #include "svdq_device.h"
 #include "svdq_launch.h"
 
@@ -32,80 +33,6 @@ namespace svdq {
 namespace {
 
 constexpr int kQaWaves = 8;
-constexpr float kMagic8 = 12582920.0f;  // 1.5 * 2^23 + 8
-
-// Max over the 8 consecutive lanes 8r .. 8r+7 that hold one token's group: xor-1 and xor-2 lane
-// exchanges inside each quad, then the mirror of the 8-lane half row (lane l <-> 7 - l).
-__device__ __forceinline__ float group_max8(float a) {
-  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, true)));
-  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, true)));
-  return fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x141, 0xF, 0xF, true)));
-}
-
-// fl(a / 7) for a >= 0 without a division: q1 = a * RN(1/7), one FMA residual and one FMA
-// correction. Checked against the IEEE quotient for every non-negative finite float (subnormals
-// included) by an exhaustive host test.
-__device__ __forceinline__ float div7(float a) {
-  constexpr float kRcp7 = 0x1.24924ap-3f;  // RN(1/7)
-  const float q1 = a * kRcp7;
-  return __builtin_fmaf(__builtin_fmaf(-7.0f, q1, a), kRcp7, q1);
-}
-
-// Quantize two groups of 8 values (xh[0..7] with scale s0, xh[8..15] with scale s1) and return
-// each packed as one word of two's-complement nibbles (element e in bits 4e..4e+3).
-//
-// Fast path: rc = v_rcp_f32(s) is within 1 ulp of 1/s for a normal s with a normal reciprocal,
-// so rc -/+ 6 ulps bracket 1/s with more than 4 ulps to spare on each side; the exact products
-// x * rc_lo and x * rc_hi then bracket fl(x / s) (which is within half an ulp of x / s), and
-// fma(x, rc_lo, M8) / fma(x, rc_hi, M8) round them to integers in one step. Equal results mean
-// every value in between, fl(x / s) included, rounds to that integer, the rule's code (no clamp
-// is needed: |fl(x / s)| <= 7 (1 + 2^-23) for a normal scale). Value positions where some lane
-// could not decide are recomputed with the IEEE division and the clamp; all of them when a scale
-// is 0, subnormal or above 2^126. f = M8 + code has code + 8 in its low byte, upper nibble zero, which packs with shifts and
-// byte permutes; a final xor turns offset binary into two's complement.
-__device__ __forceinline__ void quantize8x2(const float (&xh)[16], float s0, float s1, uint32_t& w0, uint32_t& w1) {
-  const float rc0 = __builtin_amdgcn_rcpf(s0);
-  const float rc1 = __builtin_amdgcn_rcpf(s1);
-  const float rlo0 = __uint_as_float(__float_as_uint(rc0) - 6u);
-  const float rhi0 = __uint_as_float(__float_as_uint(rc0) + 6u);
-  const float rlo1 = __uint_as_float(__float_as_uint(rc1) - 6u);
-  const float rhi1 = __uint_as_float(__float_as_uint(rc1) + 6u);
-  const uint64_t scale_bad = __ballot(!(s0 >= FLT_MIN && s0 <= 0x1p126f && s1 >= FLT_MIN && s1 <= 0x1p126f));
-  uint64_t bad = scale_bad;
-  uint64_t undecided[16];  // per value position: the lanes whose bracket straddles a boundary
-  float f[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float a = __builtin_fmaf(xh[e], e < 8 ? rlo0 : rlo1, kMagic8);
-    const float b = __builtin_fmaf(xh[e], e < 8 ? rhi0 : rhi1, kMagic8);
-    undecided[e] = __ballot(a != b);
-    bad |= undecided[e];
-    f[e] = a;
-  }
-  if (bad != 0ull) {
-    // IEEE division for the positions some lane could not decide (all of them if a scale is 0,
-    // subnormal or above 2^126).
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (scale_bad != 0ull || undecided[e] != 0ull) {
-        const float s = e < 8 ? s0 : s1;
-        float q = 0.0f;
-        if (s != 0.0f) q = fminf(fmaxf(rintf(xh[e] / s), -8.0f), 7.0f);
-        f[e] = kMagic8 + q;
-      }
-    }
-  }
-  uint32_t pr[8];  // byte 0 of pr[b] = (u[2b+1] << 4) | u[2b]
-#pragma unroll
-  for (int b = 0; b < 8; ++b) pr[b] = (__float_as_uint(f[2 * b + 1]) << 4) | __float_as_uint(f[2 * b]);
-  const uint32_t lo0 = __builtin_amdgcn_perm(pr[1], pr[0], 0x0C0C0400u);
-  const uint32_t hi0 = __builtin_amdgcn_perm(pr[3], pr[2], 0x04000C0Cu);
-  const uint32_t lo1 = __builtin_amdgcn_perm(pr[5], pr[4], 0x0C0C0400u);
-  const uint32_t hi1 = __builtin_amdgcn_perm(pr[7], pr[6], 0x04000C0Cu);
-  w0 = (lo0 | hi0) ^ 0x88888888u;
-  w1 = (lo1 | hi1) ^ 0x88888888u;
-}
-
 constexpr int kQaChunk = 6;       // groups per load schedule of a wave
 constexpr int kQaAhead = 3;       // groups in flight ahead of the computation
 constexpr int kRedCols = 4;       // rank tiles of 16 columns per step of the T reduction
@@ -117,7 +44,9 @@ __device__ __forceinline__ uint4 load_x16(const uint16_t* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p)));
 }
 
-template <int NR>
+// FMT 0: INT4 codes and float32 scales [K/64, M]; FMT 1: MXFP4 codes and E8M0 bytes [K/64, M, 2]
+// (ascale is then a byte array).
+template <int NR, int FMT>
 __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                      const float* __restrict__ inv,
                                                                      const uint16_t* __restrict__ l1t, int r,
@@ -185,15 +114,25 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
       am0 = fmaxf(am0, fmaxf(fabsf(xh[2 * e]), fabsf(xh[2 * e + 1])));
       am1 = fmaxf(am1, fmaxf(fabsf(xh[8 + 2 * e]), fabsf(xh[9 + 2 * e])));
     }
-    const float s0 = div7(group_max8(am0));
-    const float s1 = div7(group_max8(am1));
     uint32_t w0, w1;
-    quantize8x2(xh, s0, s1, w0, w1);
+    if constexpr (FMT == 0) {
+      const float s0 = div7(group_max8(am0));
+      const float s1 = div7(group_max8(am1));
+      quantize8x2(xh, s0, s1, w0, w1);
+      // scales: lanes c == 0 store token m0 + rr, lanes c == 1 token m0 + 8 + rr (one instruction)
+      if (c < 2 && (c == 0 ? ok0 : ok1)) ascale[(size_t)g * M + (c == 0 ? mh0 : mh1)] = c == 0 ? s0 : s1;
+    } else {
+      uint32_t b0, b1;
+      quantize_mx8x2(xh, am0, am1, w0, w1, b0, b1);
+      // E8M0 bytes of (group g, token, block c / 4) at (g * M + token) * 2 + c / 4: lanes c == 0, 4
+      // store token m0 + rr, lanes c == 1, 5 token m0 + 8 + rr
+      uint8_t* sb = reinterpret_cast<uint8_t*>(ascale);
+      const int cc = c & 3;
+      if (cc < 2 && (cc == 0 ? ok0 : ok1)) sb[((size_t)g * M + (cc == 0 ? mh0 : mh1)) * 2 + (c >> 2)] = (uint8_t)(cc == 0 ? b0 : b1);
+    }
     uint8_t* qp = qact + ((size_t)g * M + mh0) * 32 + 4 * c;
     if (ok0) *reinterpret_cast<uint32_t*>(qp) = w0;
     if (ok1) *reinterpret_cast<uint32_t*>(qp + 8 * 32) = w1;
-    // scales: lanes c == 0 store token m0 + rr, lanes c == 1 token m0 + 8 + rr (one instruction)
-    if (c < 2 && (c == 0 ? ok0 : ok1)) ascale[(size_t)g * M + (c == 0 ? mh0 : mh1)] = c == 0 ? s0 : s1;
     if constexpr (NR > 0) {
       *reinterpret_cast<uint4*>(tb + tw0) = uint4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]),
                                                   pack_bf16x2(xh[4], xh[5]), pack_bf16x2(xh[6], xh[7])};
@@ -293,39 +232,39 @@ __global__ __launch_bounds__(kQaWaves * 64) void quantize_act_kernel(const uint1
   }
 }
 
-template <int NR>
+template <int NR, int FMT>
 hipError_t launch_nr(const uint16_t* x, int M, int K, const float* inv, const uint16_t* l1t, int r, uint8_t* qact,
                      float* ascale, uint16_t* t, hipStream_t stream) {
   const dim3 grid((M + 15) / 16);
-  hipLaunchKernelGGL(quantize_act_kernel<NR>, grid, dim3(kQaWaves * 64), 0, stream, x, M, K, inv, l1t, r, qact, ascale,
+  hipLaunchKernelGGL((quantize_act_kernel<NR, FMT>), grid, dim3(kQaWaves * 64), 0, stream, x, M, K, inv, l1t, r, qact, ascale,
                      t);
   return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const uint16_t* x, int M, int K, const float* inv, const uint16_t* l1t, int r, uint8_t* qact,
+                      float* ascale, uint16_t* t, hipStream_t stream) {
+#define SVDQ_CASE(NR) \
+  case NR: return launch_nr<NR, FMT>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
+  switch (r / 16) {
+    SVDQ_CASE(0) SVDQ_CASE(1) SVDQ_CASE(2) SVDQ_CASE(3) SVDQ_CASE(4) SVDQ_CASE(5) SVDQ_CASE(6) SVDQ_CASE(7)
+    SVDQ_CASE(8) SVDQ_CASE(9) SVDQ_CASE(10) SVDQ_CASE(11) SVDQ_CASE(12) SVDQ_CASE(13) SVDQ_CASE(14)
+    SVDQ_CASE(15) SVDQ_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef SVDQ_CASE
 }
 
 }  // namespace
 
 hipError_t launch_quantize_act(const uint16_t* x, int M, int K, const float* inv, const uint16_t* l1t, int r,
                                uint8_t* qact, float* ascale, uint16_t* t, hipStream_t stream) {
-  switch (r / 16) {
-    case 0: return launch_nr<0>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 1: return launch_nr<1>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 2: return launch_nr<2>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 3: return launch_nr<3>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 4: return launch_nr<4>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 5: return launch_nr<5>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 6: return launch_nr<6>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 7: return launch_nr<7>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 8: return launch_nr<8>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 9: return launch_nr<9>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 10: return launch_nr<10>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 11: return launch_nr<11>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 12: return launch_nr<12>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 13: return launch_nr<13>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 14: return launch_nr<14>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 15: return launch_nr<15>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    case 16: return launch_nr<16>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_fmt<0>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
+}
+
+hipError_t launch_quantize_act_mxfp4(const uint16_t* x, int M, int K, const float* inv, const uint16_t* l1t, int r,
+                                     uint8_t* qact, uint8_t* ascale, uint16_t* t, hipStream_t stream) {
+  return launch_fmt<1>(x, M, K, inv, l1t, r, qact, reinterpret_cast<float*>(ascale), t, stream);
 }
 
 }  // namespace svdq

@@ -28,6 +28,7 @@ hipError_t launch_epi(const uint8_t* qact, const float* ascale, const uint8_t* q
 hipError_t launch_w4a4_gemm(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                             const uint16_t* t, const uint16_t* l2t, int r, const uint16_t* bias, uint16_t* y,
                             int M, int N, int K, const W4A4Epilogue& epi, hipStream_t stream) {
+  if (epi.quant_next) return launch_epi<3>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
   if (epi.gelu) return launch_epi<1>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
   if (epi.qkv_heads > 0) return launch_epi<2>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
   return launch_epi<0>(qact, ascale, qweight, wscale, t, l2t, r, bias, y, M, N, K, epi, stream);
@@ -40,7 +41,29 @@ hipError_t launch_w4a4_group_sums(const uint8_t* qact, const uint8_t* qweight, i
   const dim3 grid(tn1 - tn0 + 1, tm1 - tm0 + 1);
   hipLaunchKernelGGL((w4a4_gemm_kernel<0, true, 0>), grid, dim3(kThreads), 0, stream, qact, nullptr, qweight,
                      nullptr, nullptr, nullptr, 0, nullptr, nullptr, M, N, K, 0, 0, 0, nullptr, nullptr, nullptr, nullptr,
-                     out, m0, n0, tm, tn);
+                     out, m0, n0, tm, tn, NextLayer{});
+  return hipGetLastError();
+}
+
+namespace {
+
+// One thread per element of T: the column tiles' partials summed in tile order (deterministic).
+__global__ __launch_bounds__(256) void tpart_reduce_kernel(const float* __restrict__ tpart, int tiles_n, int M, int r,
+                                                           uint16_t* __restrict__ t) {
+  const int64_t total = (int64_t)M * r;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  float s = tpart[i];
+  for (int tn = 1; tn < tiles_n; ++tn) s += tpart[(int64_t)tn * total + i];
+  t[i] = f32_to_bf16(s);
+}
+
+}  // namespace
+
+hipError_t launch_tpart_reduce(const float* tpart, int tiles_n, int M, int r, uint16_t* t, hipStream_t stream) {
+  const int64_t total = (int64_t)M * r;
+  hipLaunchKernelGGL(tpart_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, tpart, tiles_n,
+                     M, r, t);
   return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@
 
 #include <type_traits>
 
+#include "quant_rules.h"
 #include "svdq_device.h"
 #include "svdq_launch.h"
 
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int M, int N, int K, int tiles_m, int tiles_n,
     int qkv_heads, const float* __restrict__ q_norm_w, const float* __restrict__ k_norm_w,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int32_t* __restrict__ dbg, int dm0,
-    int dn0, int dtm, int dtn) {
+    int dn0, int dtm, int dtn, NextLayer nxt) {
   __shared__ __align__(16) uint8_t lds[kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -280,38 +281,48 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
     const v4i A0 = as_v4i(unpack_chunk(apk[P].x, apk[P].y));
     const v4i A1 = as_v4i(unpack_chunk(apk[P].z, apk[P].w));
     gload_a(P, min(g + 2, G - 1));
+    // The weight operands of the column tiles are read one tile ahead into a second pair of
+    // registers: tile t + 1's LDS reads are in flight during tile t's rescale and MFMAs, so no MFMA
+    // waits for the LDS latency (with one pair, tile t + 1's reads could only start once tile t's
+    // MFMAs had consumed the registers).
+    v4i Bc0 = *reinterpret_cast<const v4i*>(st + rd_b);
+    v4i Bc1 = *reinterpret_cast<const v4i*>(st + rd_b + 16);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const v4i B0 = *reinterpret_cast<const v4i*>(st + rd_b + 32 * t * kPitch);
-      const v4i B1 = *reinterpret_cast<const v4i*>(st + rd_b + 32 * t * kPitch + 16);
+      v4i Bn0 = Bc0, Bn1 = Bc1;
+      if (t < 3) {
+        Bn0 = *reinterpret_cast<const v4i*>(st + rd_b + 32 * (t + 1) * kPitch);
+        Bn1 = *reinterpret_cast<const v4i*>(st + rd_b + 32 * (t + 1) * kPitch + 16);
+      }
       if (!first) finish_tile(g - 1, t);
-      D[t] = mfma_i8_32x32x32(A1, B1, mfma_i8_32x32x32(A0, B0, magic));
+      D[t] = mfma_i8_32x32x32(A1, Bc1, mfma_i8_32x32x32(A0, Bc0, magic));
+      Bc0 = Bn0;
+      Bc1 = Bn1;
     }
     lstore(P ^ 1, lds + S * kStageBytes);
     gload_b(P ^ 1, min(g + 3, G - 1));
     read_scales(st);
     if constexpr (!DEBUG) {
-      // Issue order: B of tile 0; A widening and its load; then per tile its rescale, the next
-      // tile's B reads and the MFMAs; between tiles 1 and 2 the next stage's widening, LDS stores
-      // and loads.
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS read: B tile 0
+      // Issue order: the B reads of tiles 0 and 1; A widening and its load; then per tile the next
+      // tile's B reads, its rescale and its MFMAs; between tiles 1 and 2 the next stage's widening,
+      // LDS stores and loads.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // LDS read: B tiles 0, 1
       __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU: widen A
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load: A
       constexpr int kRescale = first ? 0 : 33;
       // tile 0
       __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);  // VALU: rescale
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // LDS read: B tile 1
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);         // MFMA
       // tile 1
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // LDS read: B tile 2
       __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);        // VALU: widen the next B tile
       __builtin_amdgcn_sched_group_barrier(0x200, 3, 0);         // LDS write
       __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);         // global load: B, scale
       // tile 2
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // LDS read: B tile 3
       __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       // tile 3
       __builtin_amdgcn_sched_group_barrier(0x002, kRescale, 0);
@@ -387,11 +398,93 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float o = acc[t][v] + bv;
-        if constexpr (EPI == 1) o = gelu_tanh(o);
+        if constexpr (EPI == 1 || EPI == 3) o = gelu_tanh(o);
         tile[(wrow + 8 * (v >> 2) + 4 * h + (v & 3)) * kEpiPitch + 32 * t + r32] = f32_to_bf16(o);
       }
     }
     __syncthreads();
+    if constexpr (EPI == 3) {
+      // The MLP pair (the GELU/MLP path of the Diffusers blog on Nunchaku Lite): the tile holds the
+      // bf16 GELU output H, which is the next layer's input, so its activation step runs here and H
+      // is never stored. x_hat = float32(H) * inv_next; per token and group of 64 columns (two per
+      // tile: 8 consecutive lanes hold one group, 8 values each) the INT4 scale and codes of the
+      // rule, written in the next layer's group-major layout; bf16(x_hat) goes back into the tile
+      // for its down projection, whose partial sum over the tile's 128 columns goes to the
+      // workspace (summed over the column tiles in a fixed order by a second kernel).
+      const int c8 = (tid & 15) * 8;
+      const int n = n0 + c8;
+      const bool col_ok = n < N;  // N % 64 == 0: a group is entirely inside or outside
+      const int gl = (n0 >> 6) + ((tid & 15) >> 3);
+      const int c = tid & 7;
+      float iv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) iv[e] = col_ok ? nxt.inv[n + e] : 0.0f;
+#pragma unroll
+      for (int pass = 0; pass < kBM / 16; pass += 2) {
+        const int ra = 16 * pass + (tid >> 4), rb = ra + 16;
+        uint16_t* pa = tile + ra * kEpiPitch + c8;
+        uint16_t* pb = tile + rb * kEpiPitch + c8;
+        const uint4 va = *reinterpret_cast<const uint4*>(pa);
+        const uint4 vb = *reinterpret_cast<const uint4*>(pb);
+        const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+        float xh[16];
+        float am0 = 0.0f, am1 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xh[2 * e] = bf16_lo(wa[e]) * iv[2 * e];
+          xh[2 * e + 1] = bf16_hi(wa[e]) * iv[2 * e + 1];
+          xh[8 + 2 * e] = bf16_lo(wb[e]) * iv[2 * e];
+          xh[9 + 2 * e] = bf16_hi(wb[e]) * iv[2 * e + 1];
+          am0 = fmaxf(am0, fmaxf(fabsf(xh[2 * e]), fabsf(xh[2 * e + 1])));
+          am1 = fmaxf(am1, fmaxf(fabsf(xh[8 + 2 * e]), fabsf(xh[9 + 2 * e])));
+        }
+        const float s0 = div7(group_max8(am0));
+        const float s1 = div7(group_max8(am1));
+        uint32_t w0, w1;
+        quantize8x2(xh, s0, s1, w0, w1);
+        const int ma = m0 + ra, mb = m0 + rb;
+        if (col_ok) {
+          if (ma < M) *reinterpret_cast<uint32_t*>(nxt.qact + ((size_t)gl * M + ma) * 32 + 4 * c) = w0;
+          if (mb < M) *reinterpret_cast<uint32_t*>(nxt.qact + ((size_t)gl * M + mb) * 32 + 4 * c) = w1;
+          if (c == 0 && ma < M) nxt.ascale[(size_t)gl * M + ma] = s0;
+          if (c == 0 && mb < M) nxt.ascale[(size_t)gl * M + mb] = s1;
+        }
+        *reinterpret_cast<uint4*>(pa) = uint4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]),
+                                              pack_bf16x2(xh[4], xh[5]), pack_bf16x2(xh[6], xh[7])};
+        *reinterpret_cast<uint4*>(pb) = uint4{pack_bf16x2(xh[8], xh[9]), pack_bf16x2(xh[10], xh[11]),
+                                              pack_bf16x2(xh[12], xh[13]), pack_bf16x2(xh[14], xh[15])};
+      }
+      __syncthreads();
+      // Down-projection partial of the tile: wave w takes tokens 32 w .. 32 w + 31 (two 16-row
+      // MFMA tiles) and the four 32-column slabs of the tile, for each 16-column tile of the rank;
+      // MFMA 16x16x32 bf16: lane (i, j) supplies token i, values 8 j .. 8 j + 7 of the slab (A),
+      // and the L1 operand block of (rank tile, group, half) (B).
+      const int li = lane & 15, lj = lane >> 4;
+      const int Gn = N / kGroup;
+      for (int cc = 0; cc < nxt.r / 16; ++cc) {
+        v4f t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          const int f = n0 + 32 * sl;
+          if (f < N) {
+            const uint16_t* bp = nxt.l1t + (((size_t)cc * Gn + (f >> 6)) * 2 + ((f >> 5) & 1)) * 512 + lane * 8;
+            const uint4 b = *reinterpret_cast<const uint4*>(bp);
+            const uint4 a0 = *reinterpret_cast<const uint4*>(tile + (wrow + li) * kEpiPitch + 32 * sl + 8 * lj);
+            const uint4 a1 = *reinterpret_cast<const uint4*>(tile + (wrow + 16 + li) * kEpiPitch + 32 * sl + 8 * lj);
+            t0 = mfma_bf16_16x16x32(as_v8bf(a0), as_v8bf(b), t0);
+            t1 = mfma_bf16_16x16x32(as_v8bf(a1), as_v8bf(b), t1);
+          }
+        }
+        // MFMA 16x16 C layout: lane (i, j), register v -> row 4 j + v, column i
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int ma = m0 + wrow + 4 * lj + v, mb = ma + 16;
+          if (ma < M) nxt.tpart[((size_t)tn * M + ma) * nxt.r + 16 * cc + li] = t0[v];
+          if (mb < M) nxt.tpart[((size_t)tn * M + mb) * nxt.r + 16 * cc + li] = t1[v];
+        }
+      }
+      return;
+    }
     // Fused QKV (the structural-rewrite section of the Diffusers blog on Nunchaku Lite): the tile's
     // 128 columns are one head (block-uniform part: 0 = Q, 1 = K, 2 = V). Q and K rows are RMS
     // normalised per head and rotated pairwise; V passes unchanged.
@@ -434,7 +527,7 @@ hipError_t launch_nr(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
   const int tiles_n = (N + kBN - 1) / kBN;
   hipLaunchKernelGGL((w4a4_gemm_kernel<NR, false, EPI>), dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream, qa, sa,
                      qw, sw, t, l2t, r, bias, y, M, N, K, tiles_m, tiles_n, epi.qkv_heads, epi.q_norm_w, epi.k_norm_w,
-                     epi.rope_cos, epi.rope_sin, nullptr, 0, 0, 0, 0);
+                     epi.rope_cos, epi.rope_sin, nullptr, 0, 0, 0, 0, epi.next);
   return hipGetLastError();
 }
 #endif

@@ -101,3 +101,35 @@ def within_one_bf16_ulp(a: np.ndarray, b: np.ndarray, abs_floor: float) -> np.nd
     same_sign = (ab >> 15) == (bb >> 15)
     adjacent = same_sign & (np.abs(ab - bb) <= 1)
     return adjacent | (np.abs(a.astype(np.float64) - b.astype(np.float64)) <= abs_floor)
+
+
+def decode_mx_codes(packed: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """MXFP4 codes in the group-major record (byte b of (slab g, row) holds k = 64g + 2b in bits 0-3
+    and 64g + 2b + 1 in bits 4-7) -> uint8 4-bit codes [rows, K]."""
+    G = K // 64
+    b = np.asarray(packed, dtype=np.uint8).reshape(G, rows, 32)
+    out = np.empty((rows, G, 64), np.uint8)
+    out[:, :, 0::2] = (b & 0xF).transpose(1, 0, 2)
+    out[:, :, 1::2] = (b >> 4).transpose(1, 0, 2)
+    return out.reshape(rows, K)
+
+
+def decode_mx_scales(scales: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """E8M0 bytes [K/64, rows, 2] (block 2g + h of a row at (g*rows + row)*2 + h) -> uint8 [rows, K/32]."""
+    s = np.asarray(scales, dtype=np.uint8).reshape(K // 64, rows, 2)
+    return np.ascontiguousarray(s.transpose(1, 0, 2).reshape(rows, K // 32))
+
+
+def mxfp4_problem(M: int, K: int, N: int, rank: int, seed: int, resid_zero: bool = False):
+    """A seeded MXFP4 layer (same input recipe as the INT4 layers) prepared and evaluated by the oracle."""
+    cfg = synth.LayerConfig(f"mx{M}x{K}x{N}", M, K, N, rank, seed=seed, n_outliers=max(1, K // 100),
+                            outlier_scale=30.0)
+    inp = synth.make_layer_inputs(cfg)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    b = synth.f32_from_bf16_bits(inp["bias"])
+    d = oracle.svdq_decompose(x, w, rank)
+    resid = np.zeros_like(d["resid"]) if resid_zero else d["resid"]
+    out = oracle.svdq_layer_mxfp4(x, d["inv"], d["l1_bf16"], d["l2_bf16"], resid, b)
+    return {"cfg": cfg, "x_bits": inp["x"], "x": x, "bias_bits": inp["bias"], "bias": b, "inv": d["inv"],
+            "l1": d["l1_bf16"], "l2": d["l2_bf16"], "resid": resid, **out}

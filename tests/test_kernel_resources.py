@@ -28,13 +28,15 @@ def resources():
 
 def test_every_kernel_instantiation_reported(resources):
     count = lambda src: sum(1 for r in resources if r[0] == src)
-    # quantizer: one instantiation per rank r = 16 q, q = 0..16
-    assert count("quant_act.hip") == 17
-    # GEMM: the debug dump in the dispatch unit, and the 17 ranks x 3 epilogues in the generated units
-    assert count("w4a4_gemm.hip") == 1
+    # quantizer: one instantiation per rank r = 16 q, q = 0..16, for INT4 and for MXFP4
+    assert count("quant_act.hip") == 17 * 2
+    # GEMM: the debug dump and the down-projection partial sum in the dispatch unit, and the
+    # 17 ranks x 4 epilogues in the generated units
+    assert count("w4a4_gemm.hip") == 2
     gemm = [r for r in resources if r[0].startswith("w4a4_inst_") and "w4a4_gemm_kernel" in r[1]]
-    assert len(gemm) == 17 * 3
-    assert len({r[1] for r in gemm}) == 17 * 3
+    assert len(gemm) == 17 * 4
+    assert len({r[1] for r in gemm}) == 17 * 4
+    assert count("mxfp4_gemm.hip") == 17
     assert count("w4a16_gemv.hip") == 1
 
 
@@ -45,5 +47,5 @@ def test_no_kernel_uses_scratch(resources):
 
 def test_gemm_keeps_two_waves_per_simd(resources):
     for r in resources:
-        if r[0].startswith("w4a4_gemm"):
+        if r[0].startswith("w4a4_inst_") or r[0] == "mxfp4_gemm.hip":
             assert r[5] >= 2, r
