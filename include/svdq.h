@@ -247,6 +247,21 @@ int svdq_linear_w4a4_gelu_quant(const uint8_t* qact, const float* ascale, const 
                                 float* ascale_next, void* lora_act_next, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* svdq_linear_w4a4_gelu_quant for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels, with the
+ * workspace taken from a library-owned device scratch array of 64 MiB (SVDQ_NOALLOC_SCRATCH_BYTES)
+ * that each GPU holds from the first call until the process ends. Allocates nothing. Every call on
+ * one GPU uses that GPU's single scratch array: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller. Arguments as svdq_linear_w4a4_gelu_quant
+ * without the workspace; SVDQ_ERR_SHAPE if svdq_gelu_quant_workspace_bytes(M, N, r_next) exceeds the
+ * scratch size (the FLUX MLP pair, M 4608, N 12288, r 32, needs 56.6 MB). */
+#define SVDQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+int svdq_linear_w4a4_gelu_quant_noalloc(const uint8_t* qact, const float* ascale, const uint8_t* qweight,
+                                        const float* wscale, const void* lora_act, const void* l2t, int r,
+                                        const void* bias, int64_t M, int64_t N, int64_t K, const float* inv_next,
+                                        const void* l1t_next, int r_next, uint8_t* qact_next, float* ascale_next,
+                                        void* lora_act_next, void* stream);
+
 /* W4A16 projection (awq_w4a16 layers of the Diffusers blog): Y = bf16( X dequant(qweight, scales) + b ),
  * X bf16 [M, K], packed weights in the W4A16 block layout, scales bf16 [K/64, N], bias bf16 [N] or NULL.
  * Errors: SVDQ_ERR_NULL, SVDQ_ERR_SHAPE, SVDQ_ERR_ARCH, SVDQ_ERR_LAUNCH. */

@@ -9,5 +9,5 @@ from .binding import (  # noqa: F401
     load_library, status_string, svdq_abi_version, svdq_check_device, svdq_debug_group_sums, svdq_linear_w4a4,
     svdq_linear_w4a4_qkv, svdq_pack_lowrank, svdq_pack_weights, svdq_quantize_act, SVDQ_BENCH_KINDS,
     svdq_bench_unit_peak, SVDQ_FMT_MXFP4_E8M0SCALE, svdq_quantize_act_mxfp4, svdq_linear_mxfp4,
-    svdq_linear_w4a4_gelu_quant,
+    svdq_linear_w4a4_gelu_quant, svdq_linear_w4a4_gelu_quant_noalloc,
 )

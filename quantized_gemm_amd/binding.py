@@ -44,6 +44,8 @@ _SIGNATURES = {
     "svdq_gelu_quant_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "svdq_linear_w4a4_gelu_quant": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _vp, _vp, _int,
                                            _vp, _vp, _vp, _vp, _sz, _vp]),
+    "svdq_linear_w4a4_gelu_quant_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _vp,
+                                                   _vp, _int, _vp, _vp, _vp, _vp]),
     "svdq_quantize_act_mxfp4": (_int, [_vp, _i64, _i64, _vp, _vp, _int, _vp, _vp, _vp, _vp]),
     "svdq_linear_mxfp4": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64, _vp]),
 }
@@ -394,3 +396,30 @@ def svdq_linear_w4a4_gelu_quant(qact, ascale, qweight, wscale, lora_act, l2t, bi
     _check("svdq_linear_w4a4_gelu_quant", st)
     return qact_next, ascale_next, (lora_act_next if rn else None)
 
+
+def svdq_linear_w4a4_gelu_quant_noalloc(qact, ascale, qweight, wscale, lora_act, l2t, bias, inv_next, l1t_next,
+                                        qact_next, ascale_next, lora_act_next=None, stream=None):
+    """svdq_linear_w4a4_gelu_quant with the library's per-device scratch instead of a workspace; the
+    caller passes every output (nothing is allocated here or in the library)."""
+    import torch
+    G, M = ascale.shape
+    K = G * GROUP
+    N = wscale.shape[1]
+    if qact.numel() != M * K // 2:
+        raise ValueError("qact size does not match K*M/2")
+    if qweight.numel() != N * K // 2:
+        raise ValueError("qweight size does not match [N, K/2]")
+    r = 0 if l2t is None else l2t.shape[1]
+    rn = 0 if l1t_next is None else l1t_next.shape[0]
+    f32 = (torch.float32,)
+    st = load_library().svdq_linear_w4a4_gelu_quant_noalloc(
+        _dev_ptr(qact, "qact", (torch.uint8,)), _dev_ptr(ascale, "ascale", f32, (G, M)),
+        _dev_ptr(qweight, "qweight", (torch.uint8,)), _dev_ptr(wscale, "wscale", f32, (G, N)),
+        _dev_ptr(lora_act, "lora_act", _bf16(), (M, r)) if r else None,
+        _dev_ptr(l2t, "l2t", _bf16(), (N, r)) if r else None, r, _dev_ptr(bias, "bias", _bf16(), (N,)), M, N, K,
+        _dev_ptr(inv_next, "inv_next", f32, (N,)), _dev_ptr(l1t_next, "l1t_next", _bf16(), (rn, N)) if rn else None,
+        rn, _dev_ptr(qact_next, "qact_next", (torch.uint8,), (N // GROUP, M, 32)),
+        _dev_ptr(ascale_next, "ascale_next", f32, (N // GROUP, M)),
+        _dev_ptr(lora_act_next, "lora_act_next", _bf16(), (M, rn)) if rn else None, _stream(stream))
+    _check("svdq_linear_w4a4_gelu_quant_noalloc", st)
+    return qact_next, ascale_next, (lora_act_next if rn else None)

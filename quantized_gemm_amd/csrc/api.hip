@@ -50,6 +50,25 @@ int device_status() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_LAUNCH; }
 
+// Scratch of svdq_linear_w4a4_gelu_quant_noalloc: the per-column-tile float32 partials of the next
+// layer's down projection. Each GPU holds its own copy for the life of the process; host code uses
+// the address hipGetSymbolAddress returns for the current device, never the array's name.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The device address of this GPU's scratch (nullptr on failure), looked up once per device.
+void* scratch_address(int dev) {
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 int linear_w4a4(const uint8_t* qact, const float* ascale, const uint8_t* qweight, const float* wscale,
                 const void* lora_act, const void* l2t, int r, const void* bias, void* y, int64_t M, int64_t N,
                 int64_t K, const svdq::W4A4Epilogue& epi, void* stream) {
@@ -182,6 +201,30 @@ int svdq_linear_w4a4_gelu_quant(const uint8_t* qact, const float* ascale, const 
   if (rs != SVDQ_OK || r_next == 0) return rs;
   return launch_status(svdq::launch_tpart_reduce(static_cast<const float*>(workspace), (int)((N + 127) / 128), (int)M,
                                                  r_next, static_cast<uint16_t*>(lora_act_next), sh));
+}
+
+int svdq_linear_w4a4_gelu_quant_noalloc(const uint8_t* qact, const float* ascale, const uint8_t* qweight,
+                                        const float* wscale, const void* lora_act, const void* l2t, int r,
+                                        const void* bias, int64_t M, int64_t N, int64_t K, const float* inv_next,
+                                        const void* l1t_next, int r_next, uint8_t* qact_next, float* ascale_next,
+                                        void* lora_act_next, void* stream) {
+  const size_t need = svdq_gelu_quant_workspace_bytes(M, N, r_next);
+  if (r_next > 0 && (need == 0 || need > kNoallocScratchBytes)) return SVDQ_ERR_SHAPE;
+  void* ws = nullptr;
+  if (r_next > 0) {
+    const int st = device_status();
+    if (st != SVDQ_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+      (void)hipGetLastError();
+      return SVDQ_ERR_ARCH;
+    }
+    ws = scratch_address(dev);
+    if (ws == nullptr) return SVDQ_ERR_LAUNCH;
+  }
+  return svdq_linear_w4a4_gelu_quant(qact, ascale, qweight, wscale, lora_act, l2t, r, bias, M, N, K, inv_next,
+                                     l1t_next, r_next, qact_next, ascale_next, lora_act_next, ws,
+                                     r_next > 0 ? kNoallocScratchBytes : 0, stream);
 }
 
 int svdq_quantize_act_mxfp4(const void* x, int64_t M, int64_t K, const float* inv_smooth, const void* l1t, int r,
