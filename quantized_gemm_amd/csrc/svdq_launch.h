@@ -13,7 +13,7 @@ hipError_t launch_quantize_act(const uint16_t* x, int M, int K, const float* inv
 // The next layer of an MLP pair, fed from the up projection's epilogue: its smoothing reciprocals
 // [N], its L1 in the operand-block order (r*N bf16) and rank, and where its INT4 codes
 // ([N/64, M, 32] bytes), float32 scales ([N/64, M]) and the per-column-tile partial sums of its
-// down projection (float32 [N/128 rounded up, M, r], the workspace) go.
+// down projection (float32 [N/128 rounded up, r/16, M, 16], the workspace) go.
 struct NextLayer {
   const float* inv = nullptr;
   const uint16_t* l1t = nullptr;

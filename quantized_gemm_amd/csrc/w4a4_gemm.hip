@@ -48,14 +48,27 @@ hipError_t launch_w4a4_group_sums(const uint8_t* qact, const uint8_t* qweight, i
 namespace {
 
 // One thread per element of T: the column tiles' partials summed in tile order (deterministic).
+// The partials of a column tile are [rank tile cc, token m, column i] (16 floats per token and rank
+// tile); element e = (cc * M + m) * 16 + i of every tile is T[m, 16 cc + i]. Eight tiles' loads are
+// issued before they are added, in order.
 __global__ __launch_bounds__(256) void tpart_reduce_kernel(const float* __restrict__ tpart, int tiles_n, int M, int r,
                                                            uint16_t* __restrict__ t) {
   const int64_t total = (int64_t)M * r;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  float s = tpart[i];
-  for (int tn = 1; tn < tiles_n; ++tn) s += tpart[(int64_t)tn * total + i];
-  t[i] = f32_to_bf16(s);
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  float s = tpart[e];
+  int tn = 1;
+  for (; tn + 7 < tiles_n; tn += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = tpart[(int64_t)(tn + u) * total + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; tn < tiles_n; ++tn) s += tpart[(int64_t)tn * total + e];
+  const int64_t cc = e / ((int64_t)M * 16);
+  const int64_t m = (e / 16) % M;
+  t[m * r + 16 * cc + (e & 15)] = f32_to_bf16(s);
 }
 
 }  // namespace

@@ -48,7 +48,8 @@ constexpr int kBN = 128;
 constexpr int kThreads = 256;
 constexpr int kPitch = 80;  // bytes per widened LDS weight row: 64 int8 codes + 16 bytes of padding
 constexpr int kScaleOff = kBN * kPitch;                    // sa[128] then sw[128]
-constexpr int kStageBytes = kScaleOff + (kBM + kBN) * 4;
+constexpr int kGroupBytes = kScaleOff + (kBM + kBN) * 4;   // one group's widened weights and scales
+constexpr int kStageBytes = 2 * kGroupBytes;               // a stage holds a pair of groups
 constexpr int kEpiPitch = kBN + 8;                         // bf16 per row of the output staging tile
 constexpr int kStages = 3;
 constexpr int kLdsBytes = (kStages * kStageBytes > kBM * kEpiPitch * 2) ? kStages * kStageBytes : kBM * kEpiPitch * 2;
@@ -265,19 +266,22 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
     }
   };
 
-  // One K step g (C = g % 3 is the stage of group g, S = (g+1) % 3 the stage being filled,
-  // P = g & 1 the register slot): widen the wave's activation codes of group g; for each column
-  // tile, read group g's weight operands from stage C, finish the previous group's tile and issue
-  // the tile's MFMAs; store group g+1 into stage S and issue the global loads two groups ahead;
-  // finally read group g's scales (stage C) for the next step, so that their latency hides behind
-  // the barrier. Three stages make one barrier per step sufficient: the stage written in step g
-  // was last read in step g-1.
-  auto step = [&](auto cst, auto sst, auto par, int g, auto first_tag) {
+  // Groups come in pairs: pair p = groups 2p, 2p + 1 lives in stage p % 3 (slot j = g & 1 of the
+  // stage holds group g), so one barrier serves two groups. One K step g (C: the stage of g's pair;
+  // j: the slot, which is also the register slot of g's activation codes): widen the wave's
+  // activation codes of group g; for each column tile, read group g's weight operands (one tile
+  // ahead), finish the previous group's tile and issue the tile's MFMAs; store group g + 2 (the
+  // same slot of the next pair, loaded two steps before) into stage (C + 1) % 3 and issue the
+  // global loads of group g + 4; read group g's scales for the next step; after the second group
+  // of a pair, the barrier. Stage (C + 1) % 3 was last read by the pair before the previous one,
+  // so the barrier after each pair suffices.
+  auto step = [&](auto cst, auto jst, int g, auto first_tag) {
     constexpr int C = decltype(cst)::value;
-    constexpr int S = decltype(sst)::value;
-    constexpr int P = decltype(par)::value;
+    constexpr int J = decltype(jst)::value;
+    constexpr int S = (C + 1) % 3;
+    constexpr int P = J;
     constexpr bool first = decltype(first_tag)::value;
-    const uint8_t* st = lds + C * kStageBytes;
+    const uint8_t* st = lds + C * kStageBytes + J * kGroupBytes;
     const v4i A0 = as_v4i(unpack_chunk(apk[P].x, apk[P].y));
     const v4i A1 = as_v4i(unpack_chunk(apk[P].z, apk[P].w));
     gload_a(P, min(g + 2, G - 1));
@@ -299,8 +303,8 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
       Bc0 = Bn0;
       Bc1 = Bn1;
     }
-    lstore(P ^ 1, lds + S * kStageBytes);
-    gload_b(P ^ 1, min(g + 3, G - 1));
+    lstore(J, lds + S * kStageBytes + J * kGroupBytes);
+    gload_b(J, min(g + 4, G - 1));
     read_scales(st);
     if constexpr (!DEBUG) {
       // Issue order: the B reads of tiles 0 and 1; A widening and its load; then per tile the next
@@ -330,40 +334,61 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
       // (the scale reads are left to the scheduler: pinning them to the end raised the register
       // pressure past 256 VGPRs and spilled)
     }
-    __syncthreads();
+    if constexpr (J == 1) __syncthreads();
   };
 
+  // prologue: pair 0 (groups 0, 1) into stage 0, pair 1 (groups 2, 3) into the loader registers
   gload_a(0, 0);
   gload_a(1, min(1, G - 1));
   gload_b(0, 0);
   gload_b(1, min(1, G - 1));
   lstore(0, lds);
+  lstore(1, lds + kGroupBytes);
   gload_b(0, min(2, G - 1));
+  gload_b(1, min(3, G - 1));
   __syncthreads();
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  // Group g uses stage g % 3 and register slot g % 2: the pattern repeats every 6 groups.
-  step(I0(), I1(), I0(), 0, std::true_type());
+  // group g: stage (g / 2) % 3, slot g % 2; the pattern repeats every 6 groups
+  step(I0(), I0(), 0, std::true_type());
   int g = 1;
   for (; g + 5 < G; g += 6) {
-    step(I1(), I2(), I1(), g, std::false_type());
-    step(I2(), I0(), I0(), g + 1, std::false_type());
-    step(I0(), I1(), I1(), g + 2, std::false_type());
-    step(I1(), I2(), I0(), g + 3, std::false_type());
-    step(I2(), I0(), I1(), g + 4, std::false_type());
-    step(I0(), I1(), I0(), g + 5, std::false_type());
+    step(I0(), I1(), g, std::false_type());
+    step(I1(), I0(), g + 1, std::false_type());
+    step(I1(), I1(), g + 2, std::false_type());
+    step(I2(), I0(), g + 3, std::false_type());
+    step(I2(), I1(), g + 4, std::false_type());
+    step(I0(), I0(), g + 5, std::false_type());
   }
-  if (g < G) { step(I1(), I2(), I1(), g, std::false_type()); ++g; }
-  if (g < G) { step(I2(), I0(), I0(), g, std::false_type()); ++g; }
-  if (g < G) { step(I0(), I1(), I1(), g, std::false_type()); ++g; }
-  if (g < G) { step(I1(), I2(), I0(), g, std::false_type()); ++g; }
-  if (g < G) { step(I2(), I0(), I1(), g, std::false_type()); ++g; }
+  if (g < G) { step(I0(), I1(), g, std::false_type()); ++g; }
+  if (g < G) { step(I1(), I0(), g, std::false_type()); ++g; }
+  if (g < G) { step(I1(), I1(), g, std::false_type()); ++g; }
+  if (g < G) { step(I2(), I0(), g, std::false_type()); ++g; }
+  if (g < G) { step(I2(), I1(), g, std::false_type()); ++g; }
 #pragma unroll
   for (int t = 0; t < 4; ++t) finish_tile(G - 1, t);
 
   if constexpr (!DEBUG) {
+    // The MLP-pair epilogue's inputs (next layer's smoothing reciprocals of the thread's 8 columns
+    // and the L1 operands of its first rank tile) are requested here, so that their latency hides
+    // behind the up projection's own epilogue.
+    float nx_iv[8];
+    uint4 nx_b[4];
+    if constexpr (EPI == 3) {
+      const int n = n0 + (tid & 15) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) nx_iv[e] = n < N ? nxt.inv[n + e] : 0.0f;
+      if (nxt.r > 0) {
+        const int Gn = N / kGroup;
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          const int f = min(n0 + 32 * sl, N - 32);
+          nx_b[sl] = *reinterpret_cast<const uint4*>(nxt.l1t + ((size_t)(f >> 6) * 2 + ((f >> 5) & 1)) * 512 + lane * 8);
+        }
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -416,9 +441,7 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
       const bool col_ok = n < N;  // N % 64 == 0: a group is entirely inside or outside
       const int gl = (n0 >> 6) + ((tid & 15) >> 3);
       const int c = tid & 7;
-      float iv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) iv[e] = col_ok ? nxt.inv[n + e] : 0.0f;
+      const float(&iv)[8] = nx_iv;
 #pragma unroll
       for (int pass = 0; pass < kBM / 16; pass += 2) {
         const int ra = 16 * pass + (tid >> 4), rb = ra + 16;
@@ -461,26 +484,39 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
       // and the L1 operand block of (rank tile, group, half) (B).
       const int li = lane & 15, lj = lane >> 4;
       const int Gn = N / kGroup;
+      // rank tiles one after the other; the next tile's L1 operands are requested before this
+      // tile's MFMAs (the first tile's came before the up projection's epilogue)
       for (int cc = 0; cc < nxt.r / 16; ++cc) {
+        uint4 nb[4];
+        if (cc + 1 < nxt.r / 16) {
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl) {
+            const int f = min(n0 + 32 * sl, N - 32);
+            nb[sl] = *reinterpret_cast<const uint4*>(
+                nxt.l1t + (((size_t)(cc + 1) * Gn + (f >> 6)) * 2 + ((f >> 5) & 1)) * 512 + lane * 8);
+          }
+        }
         v4f t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
-          const int f = n0 + 32 * sl;
-          if (f < N) {
-            const uint16_t* bp = nxt.l1t + (((size_t)cc * Gn + (f >> 6)) * 2 + ((f >> 5) & 1)) * 512 + lane * 8;
-            const uint4 b = *reinterpret_cast<const uint4*>(bp);
+          if (n0 + 32 * sl < N) {
             const uint4 a0 = *reinterpret_cast<const uint4*>(tile + (wrow + li) * kEpiPitch + 32 * sl + 8 * lj);
             const uint4 a1 = *reinterpret_cast<const uint4*>(tile + (wrow + 16 + li) * kEpiPitch + 32 * sl + 8 * lj);
-            t0 = mfma_bf16_16x16x32(as_v8bf(a0), as_v8bf(b), t0);
-            t1 = mfma_bf16_16x16x32(as_v8bf(a1), as_v8bf(b), t1);
+            t0 = mfma_bf16_16x16x32(as_v8bf(a0), as_v8bf(nx_b[sl]), t0);
+            t1 = mfma_bf16_16x16x32(as_v8bf(a1), as_v8bf(nx_b[sl]), t1);
           }
         }
-        // MFMA 16x16 C layout: lane (i, j), register v -> row 4 j + v, column i
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) nx_b[sl] = nb[sl];
+        // MFMA 16x16 C layout: lane (i, j), register v -> row 4 j + v, column i. The workspace holds
+        // [column tile, rank tile, token, 16] floats, so each store instruction writes 4 whole
+        // consecutive 64-byte token rows of the rank tile.
+        float* tp = nxt.tpart + ((size_t)tn * (nxt.r / 16) + cc) * (size_t)M * 16;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int ma = m0 + wrow + 4 * lj + v, mb = ma + 16;
-          if (ma < M) nxt.tpart[((size_t)tn * M + ma) * nxt.r + 16 * cc + li] = t0[v];
-          if (mb < M) nxt.tpart[((size_t)tn * M + mb) * nxt.r + 16 * cc + li] = t1[v];
+          if (ma < M) tp[(size_t)ma * 16 + li] = t0[v];
+          if (mb < M) tp[(size_t)mb * 16 + li] = t1[v];
         }
       }
       return;
