@@ -179,7 +179,7 @@ def batch_timing(fn, stream, launches=200, batches=10, warm=20):
             "max": round(float(t.max()), 2), "mean": round(float(t.mean()), 2), "launches": per * batches}
 
 
-def unit_peaks(dev, stream):
+def unit_peaks(dev, stream, blocks_per_cu=4):
     """Matrix-core and vector rates of this GPU from the microbenchmarks of include/svdq_bench.h:
     achieved rate, the shader clock it ran at (s_memtime / s_memrealtime), and the rate per CU and
     clock, for the int8 and bf16 matrix shapes, the float32 outer-product shape and the float32
@@ -188,10 +188,10 @@ def unit_peaks(dev, stream):
     import quantized_gemm_amd as q
     props = torch.cuda.get_device_properties(dev)
     cus = props.multi_processor_count
-    blocks = 4 * cus
+    blocks = blocks_per_cu * cus
     clocks = torch.zeros((blocks, 2), dtype=torch.int64, device=dev)
     sink = torch.zeros(256, dtype=torch.int32, device=dev)
-    out = {"compute_units": cus}
+    out = {"compute_units": cus, "waves_per_simd": blocks_per_cu}
     for kind, (_, ops_per_inst) in q.SVDQ_BENCH_KINDS.items():
         iters = 4000 if kind == "mfma_i8_32x32x32" else 2000
         insts_per_iter = 64 if kind == "valu_fma_f32" else 16
@@ -211,6 +211,7 @@ def unit_peaks(dev, stream):
                      "ops_per_clk_per_CU": round(rate * 1e12 / (ghz * 1e9) / cus, 1),
                      "cycles_per_wave_instruction": round(ghz * 1e9 * t / (iters * insts_per_iter * blocks * 4 /
                                                                           (4 * cus)), 2)}
+    # (a block is 4 waves, one per SIMD: blocks_per_cu waves share each SIMD)
     return out
 
 
@@ -886,7 +887,9 @@ def main():
         assert torch.cuda.is_available(), "bench.py needs a HIP device"
         q.load_library()
         q.svdq_check_device()
-        print(json.dumps({"unit_peaks": unit_peaks(torch.device("cuda:0"), torch.cuda.current_stream())}), flush=True)
+        dev, st = torch.device("cuda:0"), torch.cuda.current_stream()
+        print(json.dumps({"unit_peaks": unit_peaks(dev, st),
+                          "by_waves_per_simd": {w: unit_peaks(dev, st, w) for w in (1, 2)}}), flush=True)
         return
 
     import torch

@@ -58,7 +58,7 @@ __all__ = [
     "quantize_weights_w4a4", "smooth_activations", "quantize_activations", "lowrank_down",
     "group_sums", "dequant_product", "svdq_linear", "svdq_layer", "quantize_weights_w4a16",
     "awq_linear", "gelu_tanh", "svdq_linear_gelu", "qkv_norm_rope",
-    "MX_BLOCK", "E2M1_VALUES", "e2m1_decode", "e2m1_round", "mxfp4_quantize_rows", "mxfp4_dequant",
+    "svdq_layer_naive", "MX_BLOCK", "E2M1_VALUES", "e2m1_decode", "e2m1_round", "mxfp4_quantize_rows", "mxfp4_dequant",
     "quantize_activations_mxfp4", "quantize_weights_mxfp4", "svdq_linear_mxfp4", "svdq_layer_mxfp4",
 ]
 
@@ -261,6 +261,26 @@ def svdq_layer(x, inv, l1_bf16, l2_bf16, resid, bias=None):
     qw, sw = quantize_weights_w4a4(resid)
     y64, y = svdq_linear(qa, sa, qw, sw, t, l2_bf16, bias)
     return {"qa": qa, "sa": sa, "t": t, "qw": qw, "sw": sw, "y64": y64, "y": y}
+
+
+def svdq_layer_naive(x, inv, l1_bf16, l2_bf16, resid, bias=None):
+    """The layer run the unfused way of the engine-design figure's panel (a): the 4-bit branch writes
+    its 16-bit output Y0 = bf16(dequant(Q4(X_hat) Q4(R)) + b); a separate 16-bit down projection
+    reads X again, T = bf16(X @ bf16(diag(inv) L1)) (the smoothing folded into L1, since it no longer
+    passes through the quantizer); a separate up projection reads and rewrites the 16-bit output,
+    Y = bf16(Y0 + T L2). The same quantities as svdq_layer with the two extra 16-bit roundings of
+    that form. Returns the dict of svdq_layer with "y0", "l1s", "t" and "y" of the naive form."""
+    qa, sa, _ = quantize_activations(x, inv, None)
+    qw, sw = quantize_weights_w4a4(resid)
+    y0 = dequant_product(qa, sa, qw, sw)
+    if bias is not None:
+        y0 = y0 + bias.astype(np.float64)[None, :]
+    y0 = bf16_round(y0.astype(np.float32))
+    l1s = bf16_round((inv.astype(np.float64)[:, None] * l1_bf16.astype(np.float64)).astype(np.float32))
+    t = bf16_round((x.astype(np.float64) @ l1s.astype(np.float64)).astype(np.float32))
+    y64 = y0.astype(np.float64) + t.astype(np.float64) @ l2_bf16.astype(np.float64)
+    return {"qa": qa, "sa": sa, "qw": qw, "sw": sw, "y0": y0, "l1s": l1s, "t": t, "y64": y64,
+            "y": bf16_round(y64.astype(np.float32))}
 
 
 # ----------------------------------------------------------------------------------------------

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import synth
+from guard import Guarded
 from problems import decode_qact, random_w4a4_problem, tolerance_report, within_one_bf16_ulp
 
 pytestmark = pytest.mark.gpu
@@ -83,8 +84,13 @@ def test_gelu_quant_matches_oracle_on_gpu_intermediate(gpu, M, D, F, ru, rd):
     if rd:
         a, b = q.svdq_pack_lowrank(d_dn["l1_bf16"], d_dn["l2_bf16"])
         l1t2, l2t2 = to_dev_bf16(a, gpu), to_dev_bf16(b, gpu)
-    qa2, sa2, t2 = q.svdq_linear_w4a4_gelu_quant(qa1, sa1, qw1, sw1, t1, l2t1, bias1, inv2, l1t2)
-    torch.cuda.synchronize()
+    gq, gs = Guarded((F // 64, M, 32), torch.uint8, gpu), Guarded((F // 64, M), torch.float32, gpu)
+    gt = Guarded((M, rd), torch.bfloat16, gpu) if rd else None
+    qa2, sa2, t2 = q.svdq_linear_w4a4_gelu_quant(qa1, sa1, qw1, sw1, t1, l2t1, bias1, inv2, l1t2, gq.tensor, gs.tensor,
+                                                 gt.tensor if rd else None)
+    for g, what in ((gq, "qact_next"), (gs, "ascale_next"), (gt, "lora_act_next")):
+        if g is not None:
+            g.check(what)
     ref = oracle.svdq_layer(h_gpu, d_dn["inv"], d_dn["l1_bf16"], d_dn["l2_bf16"], d_dn["resid"], b_dn)
     assert np.array_equal(decode_qact(qa2.cpu().numpy(), M, F), ref["qa"]), "next-layer codes differ"
     assert np.array_equal(sa2.cpu().numpy().view(np.uint32), np.ascontiguousarray(ref["sa"]).view(np.uint32)), \

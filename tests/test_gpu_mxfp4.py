@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import synth
+from guard import Guarded
 from problems import decode_mx_codes, decode_mx_scales, mxfp4_problem, tolerance_report, within_one_bf16_ulp
 
 pytestmark = pytest.mark.gpu
@@ -60,9 +61,18 @@ def run_layer(p, dev, rows=None):
         a, b = q.svdq_pack_lowrank(p["l1"], p["l2"])
         l1t, l2t = to_dev_bf16(a, dev), to_dev_bf16(b, dev)
     xb = p["x_bits"] if rows is None else p["x_bits"][:rows]
-    qact, ascale, t = q.svdq_quantize_act_mxfp4(to_dev_bf16(xb, dev), to_dev(p["inv"], dev), l1t)
-    y = q.svdq_linear_mxfp4(qact, ascale, to_dev(qw, dev), to_dev(sw, dev), t, l2t, to_dev_bf16(p["bias_bits"], dev))
-    torch.cuda.synchronize()
+    M, K = xb.shape
+    N = p["resid"].shape[1]
+    gq, gs = Guarded((K // 64, M, 32), torch.uint8, dev), Guarded((K // 64, M, 2), torch.uint8, dev)
+    gt = Guarded((M, r), torch.bfloat16, dev) if r else None
+    gy = Guarded((M, N), torch.bfloat16, dev)
+    qact, ascale, t = q.svdq_quantize_act_mxfp4(to_dev_bf16(xb, dev), to_dev(p["inv"], dev), l1t, gq.tensor,
+                                                gs.tensor, gt.tensor if r else None)
+    y = q.svdq_linear_mxfp4(qact, ascale, to_dev(qw, dev), to_dev(sw, dev), t, l2t, to_dev_bf16(p["bias_bits"], dev),
+                            gy.tensor)
+    for g, what in ((gq, "qact"), (gs, "ascale"), (gt, "lora_act"), (gy, "y")):
+        if g is not None:
+            g.check(what)
     return qact, ascale, t, y
 
 

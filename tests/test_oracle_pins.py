@@ -498,3 +498,31 @@ def test_qkv_rotary_is_a_complex_rotation_of_pairs():
     pn = lambda a: np.hypot(a[:, 0::2], a[:, 1::2])
     assert np.allclose(pn(rot[:, :2 * H * D]), pn(plain[:, :2 * H * D]), rtol=2 ** -6, atol=1e-6)
     assert np.array_equal(rot[:, 2 * H * D:], y[:, 2 * H * D:])
+
+
+
+def test_naive_form_reduces_to_the_fused_layer():
+    """The unfused (naive) form differs from the layer only by its two extra 16-bit roundings: with a
+    zero L1 the output is the fused layer's bit for bit (T = 0, Y = bf16(bf16(Y0))), and with unit
+    smoothing on bf16 inputs its down projection is the fused T bit for bit (diag(inv) L1 = L1 exactly,
+    bf16(X_hat) = X)."""
+    cfg = synth.LayerConfig("nv", 40, 128, 96, 16, seed=17, n_outliers=2, outlier_scale=20.0)
+    inp = synth.make_layer_inputs(cfg)
+    x = synth.f32_from_bf16_bits(inp["x"])
+    w = synth.f32_from_bf16_bits(inp["w"])
+    b = synth.f32_from_bf16_bits(inp["bias"])
+    d = oracle.svdq_decompose(x, w, cfg.rank)
+    zero_l1 = np.zeros_like(d["l1_bf16"])
+    nv = oracle.svdq_layer_naive(x, d["inv"], zero_l1, d["l2_bf16"], d["resid"], b)
+    fu = oracle.svdq_layer(x, d["inv"], zero_l1, d["l2_bf16"], d["resid"], b)
+    assert np.array_equal(nv["t"], np.zeros_like(nv["t"]))
+    assert np.array_equal(nv["y"], fu["y"])
+    ones = np.ones_like(d["inv"])
+    nv1 = oracle.svdq_layer_naive(x, ones, d["l1_bf16"], d["l2_bf16"], d["resid"], b)
+    fu1 = oracle.svdq_layer(x, ones, d["l1_bf16"], d["l2_bf16"], d["resid"], b)
+    assert np.array_equal(nv1["l1s"], d["l1_bf16"])
+    assert np.array_equal(nv1["t"], fu1["t"])
+    # and the naive output is the bf16 rounding of Y0 + T L2, Y0 being the 4-bit branch's bf16 output
+    y0 = oracle.bf16_round((oracle.dequant_product(fu1["qa"], fu1["sa"], fu1["qw"], fu1["sw"]) +
+                            b.astype(np.float64)).astype(np.float32))
+    assert np.array_equal(nv1["y0"], y0)

@@ -232,3 +232,25 @@ def test_valid_arguments_without_gpu_report_arch(lib):
     assert lib.svdq_linear_w4a4_gelu(P, P, P, P, None, None, 0, None, P, 16, 16, 64, None) == -5
     assert lib.svdq_linear_w4a4_qkv(P, P, P, P, None, None, 0, None, P, 16, 384, 64, 1, P, P, P, P, None) == -5
     assert lib.awq_linear_w4a16(P, P, P, None, P, 16, 16, 64, None) == -5
+
+
+@pytest.mark.slow
+def test_pack_full_up_shape_bit_exact_vs_oracle(lib):
+    """The weights of the FLUX MLP up projection (K 3072, N 12288: 37.7M codes), packed by the library
+    in both 4-bit formats and decoded with the documented layouts (vectorised decoder: group-major
+    records, low nibble = even k), bit-exact against the oracle."""
+    from problems import decode_mx_codes, decode_mx_scales, decode_qact
+    cfg = synth.CONFIGS["up"]
+    inp = synth.make_layer_inputs(cfg, M=64)
+    w = synth.f32_from_bf16_bits(inp["w"])
+    w[:, :3] *= 1e3                                         # columns with large groups
+    w[:64, 3] = 0.0                                         # a zero group
+    K, N = w.shape
+    qw, sw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, w)
+    oc, os_ = oracle.quantize_weights_w4a4(w)
+    assert np.array_equal(sw.view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(decode_qact(qw, N, K), np.ascontiguousarray(oc.T))
+    qm, sm = q.svdq_pack_weights(q.SVDQ_FMT_MXFP4_E8M0SCALE, w)
+    mc, ms = oracle.quantize_weights_mxfp4(w)
+    assert np.array_equal(decode_mx_codes(qm, N, K), mc)
+    assert np.array_equal(decode_mx_scales(sm, N, K), ms)
