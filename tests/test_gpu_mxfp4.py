@@ -91,9 +91,9 @@ def check(p, qact, ascale, t, y, rows=None):
 
 
 # (M, K, N, rank): one slab, an odd slab count, several tiles with ragged M and N, ranks 0 to 256,
-# and the FLUX attention shape
+# the FLUX attention shape, and ragged token counts in the quantizer's 32-token blocks
 SHAPES = [(256, 256, 512, 16), (33, 64, 48, 16), (130, 192, 272, 48), (77, 448, 144, 0), (200, 640, 400, 256),
-          (4608, 3072, 3072, 32)]
+          (4608, 3072, 3072, 32), (4113, 256, 384, 256), (4127, 192, 64, 32)]
 
 
 @pytest.mark.timeout(600)
