@@ -170,16 +170,23 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_gemm_kernel(
   // Activation loads: lane reads packed bytes [16h, 16h+16) (chunks 2h, 2h+1) of its token's group.
   // Tokens past M read the last valid token: their outputs are never stored.
   const uint32_t a_off = (uint32_t)min(m0 + wrow + r32, M - 1) * 32u + 16u * h;
-  // Loader role (block-wide): 16 packed bytes of weight row lrow, and one scale.
-  const int lrow = tid >> 1;
-  const int lhalf = tid & 1;
+  // Loader role (block-wide): 16 packed bytes (half lhalf) of weight row lrow, and one scale. Each 8
+  // lanes take 8 consecutive rows of one half, so that their 16-byte LDS stores at the 80-byte row
+  // pitch fall on distinct banks (with two halves of four rows per 8 lanes, two stores met on a
+  // bank); each 16 lanes still read 256 contiguous bytes of the weights.
+  const int lrow = (tid & 7) | ((tid >> 4) << 3);
+  const int lhalf = (tid >> 3) & 1;
   const uint32_t b_off = (uint32_t)min(n0 + lrow, N - 1) * 32u + 16u * lhalf;
   const bool s_is_a = tid < kBM;
-  const uint32_t s_off = s_is_a ? (uint32_t)min(m0 + tid, M - 1) : (uint32_t)min(n0 + tid - kBM, N - 1);
+  // weight-scale loader i = tid - kBM takes column 32 (i % 4) + i / 4 and writes slot i (consecutive
+  // lanes, consecutive 4-byte slots: no bank conflict)
+  const int sl = tid - kBM;
+  const uint32_t s_off = s_is_a ? (uint32_t)min(m0 + tid, M - 1) : (uint32_t)min(n0 + 32 * (sl & 3) + (sl >> 2), N - 1);
   const uint32_t st_b = lrow * kPitch + 32 * lhalf;
-  // Scale slot in the stage: sa of token tid, or sw of column 32 t + c stored at 4 c + t, so that
-  // a lane reads the weight scales of its column in all four column tiles with one 16-byte read.
-  const uint32_t st_s = s_is_a ? (uint32_t)tid : (uint32_t)(kBM + ((tid - kBM) & 31) * 4 + ((tid - kBM) >> 5));
+  // Scale slot in the stage: sa of token tid, or sw of column 32 t + c stored at 4 c + t (written by
+  // loader thread kBM + 4 c + t), so that a lane reads the weight scales of its column in all four
+  // column tiles with one 16-byte read.
+  const uint32_t st_s = (uint32_t)tid;
   // Operand / scale read offsets within a stage.
   const uint32_t rd_b = r32 * kPitch + 32 * h;
   const uint32_t rd_sa = kScaleOff + 4 * (wrow + 4 * h);
