@@ -124,14 +124,15 @@ __global__ __launch_bounds__(kMxThreads, 2) void mxfp4_gemm_kernel(
     const uint32_t sbytes = s_is_a ? (uint32_t)M * 2u : (uint32_t)N * 2u;
     spk[slot] = __builtin_amdgcn_raw_buffer_load_b16(mx_rsrc(sbase, sbytes), (int)s_off, 0, 0);
   };
+  // The two scale bytes: activation rows at st_sa, st_sa + 1; weight columns at st_sw, st_sw + 4.
+  // Branch-free (two byte stores either way): a branch here would split the unrolled loop into
+  // blocks, and the compiler would then sink every MFMA to the loop's end, past all its barriers.
+  const uint32_t st_s0 = s_is_a ? st_sa : st_sw;
+  const uint32_t st_s1 = s_is_a ? st_sa + 1 : st_sw + 4;
   auto lstore = [&](int slot, uint8_t* st) {
     *reinterpret_cast<uint4*>(st + st_b) = bpk[slot];
-    if (s_is_a) {
-      *reinterpret_cast<uint16_t*>(st + st_sa) = (uint16_t)spk[slot];
-    } else {
-      st[st_sw] = (uint8_t)(spk[slot] & 0xFF);
-      st[st_sw + 4] = (uint8_t)(spk[slot] >> 8);
-    }
+    st[st_s0] = (uint8_t)(spk[slot] & 0xFF);
+    st[st_s1] = (uint8_t)(spk[slot] >> 8);
   };
 
   v16f acc[4];
@@ -157,6 +158,9 @@ __global__ __launch_bounds__(kMxThreads, 2) void mxfp4_gemm_kernel(
       const uint4 B = *reinterpret_cast<const uint4*>(st + rd_b + 32 * t * kMxPitch);
       acc[t] = mfma_mxfp4(A, B, acc[t], sa_l, (sw_l >> (8 * t)) & 0xFFu);
     }
+    // The slab's MFMAs are issued here, before the next stage's stores, loads and the barrier, and
+    // run under them.
+    __builtin_amdgcn_sched_barrier(0);
     lstore(P ^ 1, lds + S * kMxStage);
     gload_b(P ^ 1, min(g + 3, G - 1));
     __syncthreads();
