@@ -14,11 +14,14 @@
 // group-major record as the INT4 layer (the 32 bytes of (slab s, row) at (s * rows + row) * 32), so
 // lane (r, h) reads bytes 16 h .. 16 h + 15 of its record; the scales are [K/64, rows, 2] bytes.
 //
-// Tiling as in the INT4 kernel: block = 128 x 128 outputs, 4 waves stacked along M, wave tile 32 x
-// 128 (four MFMA tiles), one K step per slab of 64. Activation codes go straight from global memory
-// to registers (two slabs ahead); the weight codes (shared by the 4 waves), the weight scales and
-// the activation scales of the slab are staged through LDS, three stages, one barrier per slab.
-// The epilogue adds T L2 on bf16 MFMAs into the float32 tile, adds the bias and stores bf16.
+// Tiling: block = 256 x 128 outputs, 4 waves stacked along M, wave tile 64 x 128 (2 x 4 MFMA tiles),
+// one K step per slab of 64. With no rescale on the vector unit the kernel is bound by the matrix
+// core and by LDS: each weight operand read from LDS (one 16-byte read per lane and column tile)
+// feeds two MFMAs, one per row tile of the wave, half the LDS traffic per MFMA of a 32-row wave
+// tile. Activation codes go straight from global memory to registers (two slabs ahead); the
+// weight codes (shared by the 4 waves), the weight scales and the activation scales of the slab are
+// staged through LDS, three stages, one barrier per slab. The epilogue adds T L2 on bf16 MFMAs into
+// the float32 tile, adds the bias and stores bf16.
 #include <type_traits>
 
 #include "svdq_device.h"
@@ -30,13 +33,16 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-constexpr int kMxBM = 128;
+constexpr int kMxBM = 256;
 constexpr int kMxBN = 128;
 constexpr int kMxThreads = 256;
+constexpr int kMxRowTiles = 2;                        // 32-row MFMA tiles per wave
+constexpr int kMxWaveRows = 32 * kMxRowTiles;
 constexpr int kMxPitch = 48;                          // bytes per LDS weight row: 32 + 16 (conflict-free reads)
 constexpr int kMxSwOff = kMxBN * kMxPitch;            // weight scales: 256 bytes, slot (r * 2 + h) * 4 + t
-constexpr int kMxSaOff = kMxSwOff + 2 * kMxBN;        // activation scales: 256 bytes, (row * 2 + h)
-constexpr int kMxStage = kMxSaOff + 2 * kMxBM;
+constexpr int kMxSaOff = kMxSwOff + 2 * kMxBN;        // activation scales: 512 bytes, (row * 2 + h)
+constexpr int kMxSwSpare = kMxSaOff + 2 * kMxBM;      // 256 bytes the second copy of the weight scales lands in
+constexpr int kMxStage = kMxSwSpare + 2 * kMxBN;
 constexpr int kMxStages = 3;
 constexpr int kMxEpiPitch = kMxBN + 8;                // bf16 per row of the output staging tile
 constexpr int kMxLds = (kMxStages * kMxStage > kMxBM * kMxEpiPitch * 2) ? kMxStages * kMxStage
@@ -88,58 +94,62 @@ __global__ __launch_bounds__(kMxThreads, 2) void mxfp4_gemm_kernel(
   const int G = K / kGroup;
   const int r32 = lane & 31;
   const int h = lane >> 5;
-  const int wrow = 32 * wave;
+  const int wrow = kMxWaveRows * wave;
 
   // Activation codes of the lane: bytes [16 h, 16 h + 16) of its token's slab record (tokens past M
   // read the last valid token: their outputs are never stored). Row counts below 2^27 keep every
   // per-slab byte offset within 32 bits, so the loads are buffer loads: the slab's base and size
   // in scalar registers, the lane's fixed 32-bit offset.
-  const uint32_t a_off = (uint32_t)min(m0 + wrow + r32, M - 1) * 32u + 16u * h;
-  // Loader role: 16 bytes of weight row lrow (half lhalf), and the two scale bytes of activation row
-  // tid (waves 0, 1) or weight column tid - 128 (waves 2, 3).
+  uint32_t a_off[kMxRowTiles];
+#pragma unroll
+  for (int rt = 0; rt < kMxRowTiles; ++rt)
+    a_off[rt] = (uint32_t)min(m0 + wrow + 32 * rt + r32, M - 1) * 32u + 16u * h;
+  // Loader role: 16 bytes of weight row lrow (half lhalf), the two scale bytes of activation row tid,
+  // and those of weight column tid % 128 (waves 2 and 3 store their copy in a spare slot, so the
+  // stores need no branch: a branch here would split the unrolled loop into blocks, and the
+  // compiler would then sink every MFMA to the loop's end, past all its barriers).
   const int lrow = tid >> 1;
   const int lhalf = tid & 1;
   const uint32_t b_off = (uint32_t)min(n0 + lrow, N - 1) * 32u + 16u * lhalf;
-  const bool s_is_a = __builtin_amdgcn_readfirstlane(wave) < kMxBM / kWave;
-  const uint32_t s_off = s_is_a ? (uint32_t)min(m0 + tid, M - 1) * 2u : (uint32_t)min(n0 + tid - kMxBM, N - 1) * 2u;
+  const uint32_t sa_off = (uint32_t)min(m0 + tid, M - 1) * 2u;
+  const int sc = tid & (kMxBN - 1);
+  const uint32_t sw_off = (uint32_t)min(n0 + sc, N - 1) * 2u;
   const uint32_t st_b = lrow * kMxPitch + 16 * lhalf;
   // weight column c = 32 t + rr: its byte h at slot (rr * 2 + h) * 4 + t
-  const int sc = tid - kMxBM;
-  const uint32_t st_sw = kMxSwOff + ((sc & 31) * 2) * 4 + (sc >> 5);
+  const uint32_t st_sw = (tid < kMxBN ? kMxSwOff : kMxSwSpare) + ((sc & 31) * 2) * 4 + (sc >> 5);
   const uint32_t st_sa = kMxSaOff + 2 * tid;
   const uint32_t rd_b = r32 * kMxPitch + 16 * h;
   const uint32_t rd_sw = kMxSwOff + (r32 * 2 + h) * 4;
-  const uint32_t rd_sa = kMxSaOff + (wrow + r32) * 2 + h;
+  const uint32_t rd_sa = kMxSaOff + (wrow + r32) * 2 + h;  // + 64 per row tile
 
-  uint4 apk[2], bpk[2];
-  uint32_t spk[2];
+  uint4 apk[2][kMxRowTiles], bpk[2];
+  uint32_t sapk[2], swpk[2];
   auto gload_a = [&](int slot, int g) {
-    apk[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              mx_rsrc(qa + (size_t)g * M * 32, (uint32_t)M * 32u), (int)a_off, 0, 0));
+#pragma unroll
+    for (int rt = 0; rt < kMxRowTiles; ++rt)
+      apk[slot][rt] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    mx_rsrc(qa + (size_t)g * M * 32, (uint32_t)M * 32u), (int)a_off[rt], 0, 0));
   };
   auto gload_b = [&](int slot, int g) {
     bpk[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                               mx_rsrc(qw + (size_t)g * N * 32, (uint32_t)N * 32u), (int)b_off, 0, 0));
-    const uint8_t* sbase = s_is_a ? sa + (size_t)g * M * 2 : sw + (size_t)g * N * 2;
-    const uint32_t sbytes = s_is_a ? (uint32_t)M * 2u : (uint32_t)N * 2u;
-    spk[slot] = __builtin_amdgcn_raw_buffer_load_b16(mx_rsrc(sbase, sbytes), (int)s_off, 0, 0);
+    sapk[slot] = __builtin_amdgcn_raw_buffer_load_b16(mx_rsrc(sa + (size_t)g * M * 2, (uint32_t)M * 2u), (int)sa_off, 0, 0);
+    swpk[slot] = __builtin_amdgcn_raw_buffer_load_b16(mx_rsrc(sw + (size_t)g * N * 2, (uint32_t)N * 2u), (int)sw_off, 0, 0);
   };
-  // The two scale bytes: activation rows at st_sa, st_sa + 1; weight columns at st_sw, st_sw + 4.
-  // Branch-free (two byte stores either way): a branch here would split the unrolled loop into
-  // blocks, and the compiler would then sink every MFMA to the loop's end, past all its barriers.
-  const uint32_t st_s0 = s_is_a ? st_sa : st_sw;
-  const uint32_t st_s1 = s_is_a ? st_sa + 1 : st_sw + 4;
   auto lstore = [&](int slot, uint8_t* st) {
     *reinterpret_cast<uint4*>(st + st_b) = bpk[slot];
-    st[st_s0] = (uint8_t)(spk[slot] & 0xFF);
-    st[st_s1] = (uint8_t)(spk[slot] >> 8);
+    *reinterpret_cast<uint16_t*>(st + st_sa) = (uint16_t)sapk[slot];
+    st[st_sw] = (uint8_t)(swpk[slot] & 0xFF);
+    st[st_sw + 4] = (uint8_t)(swpk[slot] >> 8);
   };
 
-  v16f acc[4];
+  v16f acc[kMxRowTiles][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int rt = 0; rt < kMxRowTiles; ++rt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.0f;
 
   // One K step g (C = g % 3: stage of slab g; S = (g + 1) % 3: stage being filled; P = g & 1:
   // register slot): the four MFMAs of slab g, then slab g + 1 into stage S and the loads two slabs
@@ -149,14 +159,21 @@ __global__ __launch_bounds__(kMxThreads, 2) void mxfp4_gemm_kernel(
     constexpr int S = decltype(sst)::value;
     constexpr int P = decltype(par)::value;
     const uint8_t* st = lds + C * kMxStage;
-    const uint4 A = apk[P];
+    uint4 A[kMxRowTiles];
+    uint32_t sa_l[kMxRowTiles];
+#pragma unroll
+    for (int rt = 0; rt < kMxRowTiles; ++rt) {
+      A[rt] = apk[P][rt];
+      sa_l[rt] = st[rd_sa + 64 * rt];
+    }
     gload_a(P, min(g + 2, G - 1));
-    const uint32_t sa_l = st[rd_sa];
     const uint32_t sw_l = *reinterpret_cast<const uint32_t*>(st + rd_sw);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint4 B = *reinterpret_cast<const uint4*>(st + rd_b + 32 * t * kMxPitch);
-      acc[t] = mfma_mxfp4(A, B, acc[t], sa_l, (sw_l >> (8 * t)) & 0xFFu);
+#pragma unroll
+      for (int rt = 0; rt < kMxRowTiles; ++rt)
+        acc[rt][t] = mfma_mxfp4(A[rt], B, acc[rt][t], sa_l[rt], (sw_l >> (8 * t)) & 0xFFu);
     }
     // The slab's MFMAs are issued here, before the next stage's stores, loads and the barrier, and
     // run under them.
@@ -196,16 +213,20 @@ __global__ __launch_bounds__(kMxThreads, 2) void mxfp4_gemm_kernel(
   if constexpr (NR > 0) {
     // T L2 with K = r in steps of 16 on 32x32x16 bf16 MFMAs; lane (r32, h) supplies rank indices
     // 16q + 8h .. +7 of token / column r32, accumulating into the same float32 tile.
-    const int mt = min(m0 + wrow + r32, M - 1);
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       const int k0 = 16 * q + 8 * h;
-      const uint4 ta = *reinterpret_cast<const uint4*>(tlr + (size_t)mt * r + k0);
+      uint4 ta[kMxRowTiles];
+#pragma unroll
+      for (int rt = 0; rt < kMxRowTiles; ++rt)
+        ta[rt] = *reinterpret_cast<const uint4*>(tlr + (size_t)min(m0 + wrow + 32 * rt + r32, M - 1) * r + k0);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int n = min(n0 + 32 * t + r32, N - 1);
         const uint4 lb = *reinterpret_cast<const uint4*>(l2t + (size_t)n * r + k0);
-        acc[t] = mfma_bf16_32x32x16(as_v8bf(ta), as_v8bf(lb), acc[t]);
+#pragma unroll
+        for (int rt = 0; rt < kMxRowTiles; ++rt)
+          acc[rt][t] = mfma_bf16_32x32x16(as_v8bf(ta[rt]), as_v8bf(lb), acc[rt][t]);
       }
     }
   }
@@ -219,8 +240,11 @@ __global__ __launch_bounds__(kMxThreads, 2) void mxfp4_gemm_kernel(
     const int n = n0 + 32 * t + r32;
     const float bv = (bias != nullptr && n < N) ? bf16_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      tile[(wrow + 8 * (v >> 2) + 4 * h + (v & 3)) * kMxEpiPitch + 32 * t + r32] = f32_to_bf16(acc[t][v] + bv);
+    for (int rt = 0; rt < kMxRowTiles; ++rt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        tile[(wrow + 32 * rt + 8 * (v >> 2) + 4 * h + (v & 3)) * kMxEpiPitch + 32 * t + r32] =
+            f32_to_bf16(acc[rt][t][v] + bv);
   }
   __syncthreads();
 #pragma unroll
