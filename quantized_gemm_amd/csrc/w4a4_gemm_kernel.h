@@ -23,9 +23,9 @@
 //     global memory (group-major layout: 1 KiB contiguous per wave and group, one 16-byte load per
 //     lane), two groups ahead, and widens them in registers.
 //   * Residual weights are shared by the 4 waves: the block loads the group's 128 columns (4 KiB,
-//     one 16-byte load per thread, two groups ahead), widens them once into LDS as int8 (rows
-//     padded to 80 bytes: conflict-free 16-byte operand reads) beside the group's 128 + 128 scales.
-//     Three LDS stages, one barrier per group.
+//     one 16-byte load per thread, four groups ahead), widens them once into LDS as int8 (rows
+//     padded to 80 bytes: conflict-free 16-byte operand reads and stores) beside the group's
+//     128 + 128 scales. Three LDS stages of two groups each, one barrier per pair of groups.
 //   * Within a wave the rescale of group g-1 is interleaved with the MFMAs of group g: the FMAs
 //     never wait for a fresh MFMA result and the matrix core runs under the VALU work.
 // Tile order: consecutive block ids land on different XCDs (round-robin dispatch), so block id b
