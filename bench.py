@@ -30,8 +30,16 @@ with the three step times.
 
 ``--mlp-pair`` times the FLUX MLP pair chained on real intermediates: the up projection (M4608,
 3072 -> 12288, r32) with the tanh-form GELU fused into its epilogue, then the down projection
-(12288 -> 3072, r32) quantizing that output. It compares the same chain with the GELU run as a
-separate bf16 pass (torch) between the two layers, and prints one JSON line.
+(12288 -> 3072, r32) quantizing that output; the pair fused across its boundary (the up
+projection's epilogue also runs the down layer's activation step, then the partial-sum reduction
+and the down GEMM); and the same chain with the GELU run as a separate bf16 pass (torch) between
+the two layers. It prints one JSON line.
+
+``--rank-sweep`` times the quantizer and the GEMM of the fused QKV projection (M4608, K3072,
+N9216) at r = 0, 32, 128 and 256, beside the unfused down projection in torch.
+
+``--mxfp4`` times the MXFP4 variant of the layer (quantizer, GEMM on the scaled FP4 matrix
+instruction, layer) beside the INT4 layer on ``--config``.
 
 ``--qkv-epilogue`` times the fused QKV projection of FLUX attention (M4608, 3072 -> 3 x 24 heads x
 128, r32) with the per-head RMS norm of Q and K and the rotary embedding in the GEMM epilogue,
