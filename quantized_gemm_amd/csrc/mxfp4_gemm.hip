@@ -20,8 +20,8 @@
 // feeds two MFMAs, one per row tile of the wave, half the LDS traffic per MFMA of a 32-row wave
 // tile. Activation codes go straight from global memory to registers (two slabs ahead); the
 // weight codes (shared by the 4 waves), the weight scales and the activation scales of the slab are
-// staged through LDS, three stages, one barrier per slab. The epilogue adds T L2 on bf16 MFMAs into
-// the float32 tile, adds the bias and stores bf16.
+// staged through LDS, three stages of two slabs each, one barrier per pair of slabs. The epilogue
+// adds T L2 on bf16 MFMAs into the float32 tile, adds the bias and stores bf16.
 #include <type_traits>
 
 #include "svdq_device.h"
@@ -42,7 +42,8 @@ constexpr int kMxPitch = 48;                          // bytes per LDS weight ro
 constexpr int kMxSwOff = kMxBN * kMxPitch;            // weight scales: 256 bytes, slot (r * 2 + h) * 4 + t
 constexpr int kMxSaOff = kMxSwOff + 2 * kMxBN;        // activation scales: 512 bytes, (row * 2 + h)
 constexpr int kMxSwSpare = kMxSaOff + 2 * kMxBM;      // 256 bytes the second copy of the weight scales lands in
-constexpr int kMxStage = kMxSwSpare + 2 * kMxBN;
+constexpr int kMxSlab = kMxSwSpare + 2 * kMxBN;        // one slab's codes and scales
+constexpr int kMxStage = 2 * kMxSlab;                  // a stage holds a pair of slabs
 constexpr int kMxStages = 3;
 constexpr int kMxEpiPitch = kMxBN + 8;                // bf16 per row of the output staging tile
 constexpr int kMxLds = (kMxStages * kMxStage > kMxBM * kMxEpiPitch * 2) ? kMxStages * kMxStage
@@ -151,22 +152,25 @@ __global__ __launch_bounds__(kMxThreads, 2) void mxfp4_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rt][t][v] = 0.0f;
 
-  // One K step g (C = g % 3: stage of slab g; S = (g + 1) % 3: stage being filled; P = g & 1:
-  // register slot): the four MFMAs of slab g, then slab g + 1 into stage S and the loads two slabs
-  // ahead. The stage written in step g was last read in step g - 1, so one barrier per step suffices.
-  auto step = [&](auto cst, auto sst, auto par, int g) {
+  // Slabs come in pairs: pair p = slabs 2p, 2p + 1 lives in stage p % 3 (slot j = g & 1 of the stage
+  // holds slab g), so one barrier serves two slabs. One K step g (C: the stage of g's pair; J: the
+  // slot, also the register slot of g's activation codes): the eight MFMAs of slab g; then slab
+  // g + 2 (the same slot of the next pair, loaded two steps before) into stage (C + 1) % 3 and the
+  // loads of slab g + 4; after the second slab of a pair, the barrier. Stage (C + 1) % 3 was last
+  // read by the pair before the previous one, so the barrier after each pair suffices.
+  auto step = [&](auto cst, auto jst, int g) {
     constexpr int C = decltype(cst)::value;
-    constexpr int S = decltype(sst)::value;
-    constexpr int P = decltype(par)::value;
-    const uint8_t* st = lds + C * kMxStage;
+    constexpr int J = decltype(jst)::value;
+    constexpr int S = (C + 1) % 3;
+    const uint8_t* st = lds + C * kMxStage + J * kMxSlab;
     uint4 A[kMxRowTiles];
     uint32_t sa_l[kMxRowTiles];
 #pragma unroll
     for (int rt = 0; rt < kMxRowTiles; ++rt) {
-      A[rt] = apk[P][rt];
+      A[rt] = apk[J][rt];
       sa_l[rt] = st[rd_sa + 64 * rt];
     }
-    gload_a(P, min(g + 2, G - 1));
+    gload_a(J, min(g + 2, G - 1));
     const uint32_t sw_l = *reinterpret_cast<const uint32_t*>(st + rd_sw);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -178,37 +182,41 @@ __global__ __launch_bounds__(kMxThreads, 2) void mxfp4_gemm_kernel(
     // The slab's MFMAs are issued here, before the next stage's stores, loads and the barrier, and
     // run under them.
     __builtin_amdgcn_sched_barrier(0);
-    lstore(P ^ 1, lds + S * kMxStage);
-    gload_b(P ^ 1, min(g + 3, G - 1));
-    __syncthreads();
+    lstore(J, lds + S * kMxStage + J * kMxSlab);
+    gload_b(J, min(g + 4, G - 1));
+    if constexpr (J == 1) __syncthreads();
   };
 
+  // prologue: pair 0 (slabs 0, 1) into stage 0, pair 1 (slabs 2, 3) into the loader registers
   gload_a(0, 0);
   gload_a(1, min(1, G - 1));
   gload_b(0, 0);
   gload_b(1, min(1, G - 1));
   lstore(0, lds);
+  lstore(1, lds + kMxSlab);
   gload_b(0, min(2, G - 1));
+  gload_b(1, min(3, G - 1));
   __syncthreads();
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  // slab g uses stage g % 3 and register slot g % 2: the pattern repeats every 6 slabs
-  int g = 0;
+  // slab g: stage (g / 2) % 3, slot g % 2; the pattern repeats every 6 slabs
+  step(I0(), I0(), 0);
+  int g = 1;
   for (; g + 5 < G; g += 6) {
-    step(I0(), I1(), I0(), g);
-    step(I1(), I2(), I1(), g + 1);
-    step(I2(), I0(), I0(), g + 2);
-    step(I0(), I1(), I1(), g + 3);
-    step(I1(), I2(), I0(), g + 4);
-    step(I2(), I0(), I1(), g + 5);
+    step(I0(), I1(), g);
+    step(I1(), I0(), g + 1);
+    step(I1(), I1(), g + 2);
+    step(I2(), I0(), g + 3);
+    step(I2(), I1(), g + 4);
+    step(I0(), I0(), g + 5);
   }
-  if (g < G) { step(I0(), I1(), I0(), g); ++g; }
-  if (g < G) { step(I1(), I2(), I1(), g); ++g; }
-  if (g < G) { step(I2(), I0(), I0(), g); ++g; }
-  if (g < G) { step(I0(), I1(), I1(), g); ++g; }
-  if (g < G) { step(I1(), I2(), I0(), g); ++g; }
+  if (g < G) { step(I0(), I1(), g); ++g; }
+  if (g < G) { step(I1(), I0(), g); ++g; }
+  if (g < G) { step(I1(), I1(), g); ++g; }
+  if (g < G) { step(I2(), I0(), g); ++g; }
+  if (g < G) { step(I2(), I1(), g); ++g; }
 
   if constexpr (NR > 0) {
     // T L2 with K = r in steps of 16 on 32x32x16 bf16 MFMAs; lane (r32, h) supplies rank indices
@@ -235,6 +243,8 @@ __global__ __launch_bounds__(kMxThreads, 2) void mxfp4_gemm_kernel(
   // 8 (v / 4) + 4 h + v % 4, column r32 of a 32 x 32 tile. The block's 128 x 128 bf16 tile goes
   // through LDS (free after the last barrier) so that each lane stores 16 contiguous bytes.
   uint16_t* tile = reinterpret_cast<uint16_t*>(lds);
+  __syncthreads();  // every wave has finished reading the stages (a loop ending on the first slab
+                    // of a pair has no barrier after it)
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int n = n0 + 32 * t + r32;
