@@ -191,7 +191,9 @@ def unit_peaks(dev, stream, blocks_per_cu=4):
     """Matrix-core and vector rates of this GPU from the microbenchmarks of include/svdq_bench.h:
     achieved rate, the shader clock it ran at (s_memtime / s_memrealtime), and the rate per CU and
     clock, for the int8 and bf16 matrix shapes, the float32 outer-product shape and the float32
-    vector FMA."""
+    vector FMA; and the SIMD-cycles of int8 MFMAs and independent FMAs issued together in the
+    W4A4 rescale's proportion, against the two parts added and overlapped. Cycles are SIMD-cycles
+    per wave instruction over the whole launch (event time x clock / instructions per SIMD)."""
     import torch
     import quantized_gemm_amd as q
     props = torch.cuda.get_device_properties(dev)
@@ -220,6 +222,13 @@ def unit_peaks(dev, stream, blocks_per_cu=4):
                      "cycles_per_wave_instruction": round(ghz * 1e9 * t / (iters * insts_per_iter * blocks * 4 /
                                                                           (4 * cus)), 2)}
     # (a block is 4 waves, one per SIMD: blocks_per_cu waves share each SIMD)
+    # The mixed kind in the W4A4 rescale's proportion, 8 int8 MFMAs to 128 FMAs per wave: its
+    # SIMD-cycles against the two parts run alone, added and overlapped.
+    m8 = 8 * out["mfma_i8_32x32x32"]["cycles_per_wave_instruction"]
+    f128 = 128 * out["valu_fma_f32"]["cycles_per_wave_instruction"]
+    out["mix_i8_fma"] = {"cycles_per_8_mfma_and_128_fma": round(8 * out["mix_i8_fma"]["cycles_per_wave_instruction"], 1),
+                         "parts_added": round(m8 + f128, 1), "parts_overlapped": round(max(m8, f128), 1),
+                         "clock_GHz": out["mix_i8_fma"]["clock_GHz"]}
     return out
 
 

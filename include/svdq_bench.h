@@ -18,12 +18,15 @@ enum svdq_bench_kind {
   SVDQ_BENCH_MFMA_I8_32X32X32 = 0,    /* v_mfma_i32_32x32x32_i8: 2*32*32*32 int8 ops each */
   SVDQ_BENCH_MFMA_BF16_32X32X16 = 1,  /* v_mfma_f32_32x32x16_bf16: 2*32*32*16 flops each */
   SVDQ_BENCH_MFMA_F32_32X32X1_2B = 2, /* v_mfma_f32_32x32x1_2b_f32: two 32x32 outer products, 4096 flops */
-  SVDQ_BENCH_VALU_FMA_F32 = 3         /* v_fma_f32 on 64 lanes: 128 flops each */
+  SVDQ_BENCH_VALU_FMA_F32 = 3,        /* v_fma_f32 on 64 lanes: 128 flops each */
+  SVDQ_BENCH_MIX_I8_FMA = 4           /* per 16 instructions: 16 int8 MFMAs as above plus 256
+                                         independent v_fma_f32 (the W4A4 rescale's proportion) */
 };
 
 /* Launch `blocks` blocks of 256 threads (4 waves) on `stream`; every wave issues
  * iters * 16 instructions of the chosen kind in four independent chains (VALU: iters * 64 FMAs
- * in sixteen chains) and touches no memory in its loop. Block b writes clocks[2b] = shader-clock
+ * in sixteen chains; MIX: iters * 16 MFMAs and iters * 256 FMAs, interleaved) and touches no
+ * memory in its loop. Block b writes clocks[2b] = shader-clock
  * cycles (s_memtime) and clocks[2b + 1] = 100 MHz real-time ticks (s_memrealtime) elapsed
  * around its loop. clocks: device memory, 2*blocks uint64; sink: device memory, 256 int32, never
  * written in practice (it keeps the results live). Asynchronous; allocates nothing.

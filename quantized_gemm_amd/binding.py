@@ -293,7 +293,8 @@ def svdq_debug_group_sums(qact, qweight, N: int, m0: int, n0: int, tm: int, tn: 
 
 
 SVDQ_BENCH_KINDS = {"mfma_i8_32x32x32": (0, 2 * 32 * 32 * 32), "mfma_bf16_32x32x16": (1, 2 * 32 * 32 * 16),
-                    "mfma_f32_32x32x1_2b": (2, 2 * 2 * 32 * 32), "valu_fma_f32": (3, 2 * 64)}
+                    "mfma_f32_32x32x1_2b": (2, 2 * 2 * 32 * 32), "valu_fma_f32": (3, 2 * 64),
+                    "mix_i8_fma": (4, 2 * 32 * 32 * 32)}
 
 
 def svdq_bench_unit_peak(kind: str, blocks: int, iters: int, clocks, sink, stream=None) -> None:

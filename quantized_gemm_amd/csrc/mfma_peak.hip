@@ -1,6 +1,8 @@
 // Microbenchmarks of the gfx950 execution units that bound the SVDQuant kernels: the dense int8
 // matrix-core rate (the denominator of the W4A4 product's roofline), the bf16 and float32 matrix
-// shapes used by the low-rank epilogue and the rescale, and the float32 vector FMA rate.
+// shapes used by the low-rank epilogue and the rescale, the float32 vector FMA rate, and the two
+// mixed in the W4A4 kernel's proportion (8 int8 MFMAs to 128 FMAs, independent of each other), which
+// shows whether a SIMD overlaps its matrix and vector work.
 //
 // Each kernel keeps four independent accumulator chains per wave (no dependent-issue stalls),
 // touches no memory in its loop, and records per block the elapsed shader clock (s_memtime) and
@@ -68,6 +70,36 @@ __global__ __launch_bounds__(256) void peak_kernel(int iters, unsigned long long
     }
 #pragma unroll
     for (int v = 0; v < 32; ++v) fsum += c0[v] + c1[v] + c2[v] + c3[v];
+  } else if constexpr (KIND == SVDQ_BENCH_MIX_I8_FMA) {
+    // per round: four int8 MFMAs (four chains) and 64 FMAs (sixteen chains), interleaved
+    const v4i a = {lane, lane * 3, lane * 5, lane * 7};
+    const v4i b = {lane * 11, lane * 13, lane * 17, lane * 19};
+    v16i c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    float f[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f[e] = (float)(lane + e);
+    const float m = 0.999f + 1e-9f * (float)lane, s = 1e-3f * (float)(lane + 1);
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c0, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) f[e] = __builtin_fmaf(f[e], m, s);
+        c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c1, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) f[e] = __builtin_fmaf(f[e], m, s);
+        c2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c2, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) f[e] = __builtin_fmaf(f[e], m, s);
+        c3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c3, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) f[e] = __builtin_fmaf(f[e], m, s);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) isum += c0[v] ^ c1[v] ^ c2[v] ^ c3[v];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) fsum += f[e];
   } else if constexpr (KIND == SVDQ_BENCH_VALU_FMA_F32) {
     // 16 independent FMA chains per lane (one instruction each per round)
     float f[16];
@@ -114,6 +146,9 @@ extern "C" int svdq_bench_unit_peak(int kind, int blocks, int iters, unsigned lo
       break;
     case SVDQ_BENCH_VALU_FMA_F32:
       hipLaunchKernelGGL(svdq::peak_kernel<SVDQ_BENCH_VALU_FMA_F32>, grid, block, 0, st, iters, clocks, sink);
+      break;
+    case SVDQ_BENCH_MIX_I8_FMA:
+      hipLaunchKernelGGL(svdq::peak_kernel<SVDQ_BENCH_MIX_I8_FMA>, grid, block, 0, st, iters, clocks, sink);
       break;
     default:
       return -4;
