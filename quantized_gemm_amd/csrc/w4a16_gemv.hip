@@ -16,10 +16,12 @@
 // Work split. X is tiny and read by every block, so it is loaded once per block, not once per
 // column tile: a block of kAwqWaves waves owns one 16-token row tile, wave w owns a slice of
 // kAwqPer consecutive groups of K (a chunk of kAwqWaves * kAwqPer groups at a time), and keeps
-// its slice of X and the 136 * Sx corrections in registers for the block's column tiles
-// t = blockIdx.x, blockIdx.x + gridDim.x, ... (up to kAwqMaxTiles per pass). The grid is about one
-// block per CU. Each wave keeps the weight loads of the next two tiles in flight while it computes
-// one, so the data of a CU's first tiles arrive, and are used, while the rest still streams in.
+// its slice of X and the 136 * Sx corrections in registers for the block's column tiles, a
+// contiguous range of them (up to kAwqMaxTiles per pass). The grid is about one block per CU.
+// Each wave keeps the weight loads of the next two tiles in flight while it computes one, so the
+// data of a CU's first tiles arrive, and are used, while the rest still streams in. (Measured on
+// the adaLN projection, M 16, K 3072, N 18432: 12 waves of 4 groups instead of 8 of 6, 11.8 ->
+// 11.1 us; contiguous tile ranges instead of tiles strided by the grid, -> 10.7 us.)
 // The partial tiles of the waves are summed in LDS in a fixed order (deterministic); wave s sums
 // tile s, adds the bias and stores bf16, so the tiles of a pass are finished in parallel.
 #include "svdq_device.h"
@@ -29,8 +31,8 @@ namespace svdq {
 
 namespace {
 
-constexpr int kAwqWaves = 8;
-constexpr int kAwqPer = 6;        // groups per wave and K chunk (even: groups come in pairs)
+constexpr int kAwqWaves = 12;
+constexpr int kAwqPer = 4;        // groups per wave and K chunk (even: groups come in pairs)
 constexpr int kAwqMaxTiles = 5;   // column tiles accumulated per pass over K
 constexpr int kAwqBlocks = 256;   // target resident blocks (one per CU)
 
@@ -86,8 +88,10 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
   const int m0 = blockIdx.y * 16;
   const int G = K / kGroup;
   const int NT = N / 16;
-  // this block's column tiles: blockIdx.x + s * gridDim.x for s < nts
-  const int nts = (NT - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  // this block's column tiles: t_first + s for s < nts (the grid splits the NT tiles into
+  // contiguous ranges whose sizes differ by at most one)
+  const int t_first = (int)(((long long)blockIdx.x * NT) / (int)gridDim.x);
+  const int nts = (int)((((long long)blockIdx.x + 1) * NT) / (int)gridDim.x) - t_first;
   // rows past M read the last row; their results are not stored
   const uint16_t* xrow = x + (size_t)min(m0 + i, M - 1) * K;
   const uint4 ones4 = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
       TileLoad tl[kAwqMaxTiles];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        if (s < nb) load_tile(tl[s], qw, scales, (int)blockIdx.x + (tb + s) * (int)gridDim.x, gb, G, N, lane, i);
+        if (s < nb) load_tile(tl[s], qw, scales, t_first + tb + s, gb, G, N, lane, i);
       v4f corr[kAwqPer];
 #pragma unroll
       for (int q = 0; q < kAwqPer; ++q) {
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
 #pragma unroll
       for (int s = 0; s < kAwqMaxTiles; ++s) {
         if (s >= nb) break;
-        if (s + 2 < kAwqMaxTiles && s + 2 < nb) load_tile(tl[s + 2], qw, scales, (int)blockIdx.x + (tb + s + 2) * (int)gridDim.x, gb, G, N, lane, i);
+        if (s + 2 < kAwqMaxTiles && s + 2 < nb) load_tile(tl[s + 2], qw, scales, t_first + tb + s + 2, gb, G, N, lane, i);
 #pragma unroll
         for (int q = 0; q < kAwqPer; ++q) {
           if (q >= ng) break;
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(kAwqWaves * 64) void w4a16_kernel(const uint16_t* _
 #pragma unroll
         for (int v = 0; v < 4; ++v) a[v] = a[v] + p[v];
       }
-      const int n = ((int)blockIdx.x + (tb + s) * (int)gridDim.x) * 16 + i;
+      const int n = (t_first + tb + s) * 16 + i;
       const float b = bias != nullptr ? bf16_to_f32(bias[n]) : 0.0f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
