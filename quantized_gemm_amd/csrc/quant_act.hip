@@ -317,16 +317,18 @@ int device_cus() {
 // Block shape per rank and token count (timed on MI355X at M = 4096 and 4608, K = 3072):
 //   * While the 16-token blocks fit one per CU, one token tile per block: the load pipeline 1 group
 //     deep at four waves per SIMD for r <= 32 (the registers allow it), 3 groups deep otherwise.
-//   * With more 16-token blocks than CUs and r > 0, two token tiles per block: from r = 64 on a
+//   * With more 16-token blocks than CUs and r >= 32, two token tiles per block: from r = 64 on a
 //     block needs more than 128 VGPRs per lane, so only one block fits per CU and the blocks past
 //     the CU count would run as a second round; 32-token blocks all run in one round, and every L1
 //     operand load serves both tiles (half the L1 traffic). M = 4608: r = 128 28.8 -> 21.3 us,
-//     r = 256 44.0 -> 31.3 us, r = 32 16.4 -> 15.0 us; at r = 0 one tile stays faster.
+//     r = 256 44.0 -> 31.3 us, r = 32 16.2 -> 15.0 us; at r = 0 and r = 16 one tile stays faster
+//     (r = 16: 13.6 against 14.7 us).
 template <int NR, int FMT>
 hipError_t launch_rank(const uint16_t* x, int M, int K, const float* inv, const uint16_t* l1t, int r, uint8_t* qact,
                        float* ascale, uint16_t* t, hipStream_t stream) {
   if constexpr (NR > 0) {
-    if ((M + 15) / 16 > device_cus()) return launch_nr<NR, FMT, 2, 1, 2>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
+    if (NR >= 2 && (M + 15) / 16 > device_cus())
+      return launch_nr<NR, FMT, 2, 1, 2>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
   }
   if constexpr (NR <= 2) {
     return launch_nr<NR, FMT, 1, 1, 4>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
