@@ -6,7 +6,8 @@
 // per-(token, 64-group) absmax with a cross-lane reduction, writes the packed INT4 codes and
 // float32 scales, and feeds bf16(X_hat) to bf16 MFMAs that accumulate T = X_hat L1 in float32.
 //
-// Work split: one block = 16 or 32 tokens (one or two token tiles) x the whole K, 8 waves; wave w
+// Work split: one block = 16, 24 or 32 tokens (one or two token tiles, the second possibly half
+// full) x the whole K, 8 waves; wave w
 // takes a contiguous eighth of the groups for every token tile of the block; its X loads (the HBM
 // stream) run one to three groups ahead of the computation. The launcher picks the shape from the
 // rank and the token count.
@@ -49,9 +50,11 @@ __device__ __forceinline__ uint4 load_x16(const uint16_t* p) {
 }
 
 // FMT 0: INT4 codes and float32 scales [K/64, M]; FMT 1: MXFP4 codes and E8M0 bytes [K/64, M, 2]
-// (ascale is then a byte array). TT: 16-token tiles per block (and per wave); AHEAD: groups whose
-// X loads are in flight ahead of the computation (AHEAD = kQaChunk issues a chunk's loads at once).
-template <int NR, int FMT, int TT, int AHEAD, int MINW>
+// (ascale is then a byte array). TT: 16-token tiles per block (and per wave); HALF: the last tile
+// holds only its first 8 tokens (a 24-token block with TT = 2), whose quantization then takes half
+// the vector work; AHEAD: groups whose X loads are in flight ahead of the computation (AHEAD =
+// kQaChunk issues a chunk's loads at once).
+template <int NR, int FMT, int TT, int AHEAD, int MINW, bool HALF>
 __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                                      const float* __restrict__ inv,
                                                                      const uint16_t* __restrict__ l1t, int r,
@@ -60,13 +63,15 @@ __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const
                                                                      uint16_t* __restrict__ tout) {
   static_assert(TT == 1 || TT == 2, "one or two token tiles per block");
   static_assert(AHEAD >= 1 && AHEAD <= kQaChunk, "loads run at most one chunk ahead");
-  constexpr int kTok = 16 * TT;
+  static_assert(!HALF || (TT == 2 && FMT == 0), "a half last tile only in two-tile INT4 blocks");
+  constexpr int kTok = 16 * TT - (HALF ? 8 : 0);
   constexpr int kNR = NR > 0 ? NR : 1;
   // L1 operand tiles in flight per group: all of them with one token tile; with two token tiles
   // and large ranks, a ring of 4 rank tiles
   constexpr int kBRing = (TT == 2 && NR >= 12) ? 2 : (TT == 2 && NR >= 6) ? 4 : NR;
   constexpr int kRedBytes = kQaWaves * kRedCols * kWave * 16;
-  constexpr int kTBytes = NR > 0 ? kQaWaves * kTok * kTPitch : 16;
+  // a wave's operand slice has 16 rows per token tile (the MFMA reads all 16 of a half tile too)
+  constexpr int kTBytes = NR > 0 ? kQaWaves * 16 * TT * kTPitch : 16;
   __shared__ __align__(16) uint8_t lds[kTBytes > kRedBytes ? kTBytes : kRedBytes];
 
   const int lane = threadIdx.x & 63;
@@ -92,7 +97,8 @@ __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       mh[tt][hf] = m0 + 16 * tt + 8 * hf + rr;
-      ok[tt][hf] = mh[tt][hf] < M;
+      // the second half of a half tile belongs to the next block
+      ok[tt][hf] = mh[tt][hf] < M && !(HALF && tt == TT - 1 && hf == 1);
       // tokens past M read the last valid token; their results are not stored
       xr[tt][hf] = x + (size_t)min(mh[tt][hf], M - 1) * K + 8 * c;
     }
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const
   // m0 + 16 tt + i, values 8j .. 8j+7 and 32+8j .. 32+8j+7; bf16(x_hat) reaches it through the
   // wave's LDS slice (written in the quantization layout, read in the operand layout). With two
   // token tiles every L1 operand load feeds both tiles' MFMAs.
-  uint8_t* tb = lds + wave * kTok * kTPitch;
+  uint8_t* tb = lds + wave * 16 * TT * kTPitch;
   const uint32_t tw = rr * kTPitch + 16 * c;                       // + (16 tt + 8 hf) rows
   const uint32_t trd = (lane & 15) * kTPitch + 16 * (lane >> 4);  // + 16 tt rows, + 64 for 32 + 8j
 
@@ -124,7 +130,8 @@ __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) p[tt][hf] = load_x16(xr[tt][hf] + g * kGroup);
+      for (int hf = 0; hf < 2; ++hf)
+        if (!(HALF && tt == TT - 1 && hf == 1)) p[tt][hf] = load_x16(xr[tt][hf] + g * kGroup);
   };
 
   // One group: per token tile smoothing, absmax, scale, codes, stores and the bf16 operand slice;
@@ -133,6 +140,33 @@ __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const
     const float iv[8] = {ivv[0].x, ivv[0].y, ivv[0].z, ivv[0].w, ivv[1].x, ivv[1].y, ivv[1].z, ivv[1].w};
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
+      if (HALF && tt == TT - 1) {
+        // the half tile: tokens m0 + 16 tt + rr only (half 0 of the load layout)
+        const uint32_t pw[4] = {p[tt][0].x, p[tt][0].y, p[tt][0].z, p[tt][0].w};
+        float xh[8];
+        float am0 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xh[2 * e] = bf16_lo(pw[e]) * iv[2 * e];
+          xh[2 * e + 1] = bf16_hi(pw[e]) * iv[2 * e + 1];
+          am0 = fmaxf(am0, fmaxf(fabsf(xh[2 * e]), fabsf(xh[2 * e + 1])));
+        }
+        const int mh0 = mh[tt][0];
+        const bool ok0 = ok[tt][0];
+        const float s0 = div7(group_max8(am0));
+        uint32_t w0;
+        quantize8x1(xh, s0, w0);
+        if (c == 0 && ok0) ascale[(size_t)g * M + mh0] = s0;
+        if (ok0) *reinterpret_cast<uint32_t*>(qact + ((size_t)g * M + mh0) * 32 + 4 * c) = w0;
+        if constexpr (NR > 0) {
+          // rows 8..15 of this tile's operand slice keep stale values: they only reach MFMA rows
+          // (tokens of the next block) whose T is not stored
+          *reinterpret_cast<uint4*>(tb + tw + 16 * tt * kTPitch) =
+              uint4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]), pack_bf16x2(xh[4], xh[5]),
+                    pack_bf16x2(xh[6], xh[7])};
+        }
+        continue;
+      }
       const uint32_t pw[8] = {p[tt][0].x, p[tt][0].y, p[tt][0].z, p[tt][0].w,
                               p[tt][1].x, p[tt][1].y, p[tt][1].z, p[tt][1].w};
       float xh[16];
@@ -276,21 +310,23 @@ __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const
             s0 = w == 0 ? p[2 * hv] : s0 + p[2 * hv];
             s1 = w == 0 ? p[2 * hv + 1] : s1 + p[2 * hv + 1];
           }
-          const int row = m0 + 16 * tt + 4 * (l >> 4) + 2 * hv;
+          const int rb = 16 * tt + 4 * (l >> 4) + 2 * hv;  // row within the block
+          const int row = m0 + rb;
           const int col = 16 * (c0 + cc) + (l & 15);
-          if (row < M) tout[(size_t)row * r + col] = f32_to_bf16(s0);
-          if (row + 1 < M) tout[(size_t)(row + 1) * r + col] = f32_to_bf16(s1);
+          if (row < M && rb < kTok) tout[(size_t)row * r + col] = f32_to_bf16(s0);
+          if (row + 1 < M && rb + 1 < kTok) tout[(size_t)(row + 1) * r + col] = f32_to_bf16(s1);
         }
       }
     }
   }
 }
 
-template <int NR, int FMT, int TT, int AHEAD, int MINW>
+template <int NR, int FMT, int TT, int AHEAD, int MINW, bool HALF = false>
 hipError_t launch_nr(const uint16_t* x, int M, int K, const float* inv, const uint16_t* l1t, int r, uint8_t* qact,
                      float* ascale, uint16_t* t, hipStream_t stream) {
-  const dim3 grid((M + 16 * TT - 1) / (16 * TT));
-  hipLaunchKernelGGL((quantize_act_kernel<NR, FMT, TT, AHEAD, MINW>), grid, dim3(kQaWaves * 64), 0, stream, x, M, K, inv,
+  constexpr int kTok = 16 * TT - (HALF ? 8 : 0);
+  const dim3 grid((M + kTok - 1) / kTok);
+  hipLaunchKernelGGL((quantize_act_kernel<NR, FMT, TT, AHEAD, MINW, HALF>), grid, dim3(kQaWaves * 64), 0, stream, x, M, K, inv,
                      l1t, r, qact, ascale, t);
   return hipGetLastError();
 }
@@ -323,12 +359,22 @@ int device_cus() {
 //     operand load serves both tiles (half the L1 traffic). M = 4608: r = 128 28.8 -> 21.3 us,
 //     r = 256 44.0 -> 31.3 us, r = 32 16.2 -> 15.0 us; at r = 0 and r = 16 one tile stays faster
 //     (r = 16: 13.6 against 14.7 us).
+//   * For r = 32 .. 64 (INT4), 24-token blocks (the second tile holds 8 tokens) while they still
+//     fit one per CU: a block's time follows its 8-token rows of vector work (two rows ~10.6 us,
+//     four ~15 us at K = 3072), so three rows on more CUs beat four on fewer. r = 32: M = 4608
+//     15.1 -> 13.8 us, M = 6000 15.7 -> 14.7 us; r = 64, M = 4608: 18.8 -> 18.1 us. At r >= 128
+//     the gain is at most 3% and at M = 6000, r = 128 it is a loss, so those keep 32 tokens.
 template <int NR, int FMT>
 hipError_t launch_rank(const uint16_t* x, int M, int K, const float* inv, const uint16_t* l1t, int r, uint8_t* qact,
                        float* ascale, uint16_t* t, hipStream_t stream) {
   if constexpr (NR > 0) {
-    if (NR >= 2 && (M + 15) / 16 > device_cus())
+    if (NR >= 2 && (M + 15) / 16 > device_cus()) {
+      if constexpr (FMT == 0 && NR >= 2 && NR <= 4) {
+        if ((M + 23) / 24 <= device_cus())
+          return launch_nr<NR, FMT, 2, 1, 2, true>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
+      }
       return launch_nr<NR, FMT, 2, 1, 2>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
+    }
   }
   if constexpr (NR <= 2) {
     return launch_nr<NR, FMT, 1, 1, 4>(x, M, K, inv, l1t, r, qact, ascale, t, stream);

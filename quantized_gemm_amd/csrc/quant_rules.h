@@ -86,6 +86,42 @@ __device__ __forceinline__ void quantize8x2(const float (&xh)[16], float s0, flo
   w1 = (lo1 | hi1) ^ 0x88888888u;
 }
 
+// The same rule for one group of 8 values (xh[0..7], scale s0): the half token tile of a block
+// whose last tile holds 8 tokens.
+__device__ __forceinline__ void quantize8x1(const float (&xh)[8], float s0, uint32_t& w0) {
+  const float rc0 = __builtin_amdgcn_rcpf(s0);
+  const float rlo0 = __uint_as_float(__float_as_uint(rc0) - 6u);
+  const float rhi0 = __uint_as_float(__float_as_uint(rc0) + 6u);
+  const uint64_t scale_bad = __ballot(!(s0 >= FLT_MIN && s0 <= 0x1p126f));
+  uint64_t bad = scale_bad;
+  uint64_t undecided[8];
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float a = __builtin_fmaf(xh[e], rlo0, kMagic8);
+    const float b = __builtin_fmaf(xh[e], rhi0, kMagic8);
+    undecided[e] = __ballot(a != b);
+    bad |= undecided[e];
+    f[e] = a;
+  }
+  if (bad != 0ull) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (scale_bad != 0ull || undecided[e] != 0ull) {
+        float q = 0.0f;
+        if (s0 != 0.0f) q = fminf(fmaxf(rintf(xh[e] / s0), -8.0f), 7.0f);
+        f[e] = kMagic8 + q;
+      }
+    }
+  }
+  uint32_t pr[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) pr[b] = (__float_as_uint(f[2 * b + 1]) << 4) | __float_as_uint(f[2 * b]);
+  const uint32_t lo0 = __builtin_amdgcn_perm(pr[1], pr[0], 0x0C0C0400u);
+  const uint32_t hi0 = __builtin_amdgcn_perm(pr[3], pr[2], 0x04000C0Cu);
+  w0 = (lo0 | hi0) ^ 0x88888888u;
+}
+
 // ---- MXFP4 (the 4-bit float variant): E2M1 codes, one E8M0 scale per block of 32 along K ----
 // Max over the 4 consecutive lanes 4r .. 4r+3 (one token's block of 32 in the load layout).
 __device__ __forceinline__ float block_max4(float a) {

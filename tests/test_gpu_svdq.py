@@ -150,11 +150,14 @@ def test_w4a4_layer_parity(gpu, name, rank):
 
 # (M, K, N, rank): 1, 2, 7, 10, 16 and 50 groups (fewer groups than waves, every tail length of the
 # GEMM's six-step loop, a quantizer chunk that is full then partial), ragged M and N, ranks 0 to 112;
-# then token counts above 256 16-token tiles, where the quantizer runs 32-token blocks, with a last
-# block holding 1, 17 and 31 tokens (its second tile empty, one token, 15 tokens)
+# then token counts above 256 16-token tiles (on a 256-CU MI355X): at r = 32 .. 64 the quantizer runs
+# 24-token blocks (second tile half full), with a last block holding 17, 8, 20 and 23 tokens (its
+# half tile with one token, empty, four and seven tokens); at r >= 128 32-token blocks, with a last
+# block holding 17 and 31 tokens (its second tile one token, 15 tokens)
 SMALL_SHAPES = [(33, 64, 48, 16), (130, 128, 272, 48), (77, 448, 144, 0), (200, 640, 400, 112),
                 (16, 1024, 1040, 64), (40, 3200, 160, 32),
-                (4097, 256, 128, 32), (4113, 128, 272, 128), (4127, 320, 272, 256)]
+                (4097, 256, 128, 32), (4112, 192, 144, 32), (4100, 128, 160, 64), (4127, 64, 128, 48),
+                (4113, 128, 272, 128), (4127, 320, 272, 256)]
 
 
 @pytest.mark.parametrize("M,K,N,rank", SMALL_SHAPES, ids=[f"M{m}K{k}N{n}r{r}" for m, k, n, r in SMALL_SHAPES])
