@@ -137,3 +137,44 @@ def test_mxfp4_activation_edge_values(gpu):
         torch.cuda.synchronize()
         assert np.array_equal(decode_mx_codes(qact.cpu().numpy(), M, K), qa)
         assert np.array_equal(decode_mx_scales(ascale.cpu().numpy(), M, K), sa)
+
+
+# (M, K, N, sa, sw): ragged token and column counts; every activation block scale 2^sa, every weight
+# block scale 2^sw
+EXACT_SHAPES = [(200, 512, 272, -3, -5), (33, 3072, 48, 2, -7), (4127, 192, 64, 0, 0)]
+
+
+@pytest.mark.parametrize("M,K,N,sa,sw", EXACT_SHAPES, ids=[f"M{m}K{k}N{n}" for m, k, n, _, _ in EXACT_SHAPES])
+def test_mxfp4_product_exact_with_grid_inputs(gpu, M, K, N, sa, sw):
+    """Inputs that are E2M1 values times one power of two per operand, with a +-6 in every block of 32,
+    so the rule reproduces them exactly (scale 2^s, element x / 2^s). Every product is a multiple of
+    2^(sa+sw-2) and |sum| <= 36 K of 2^(sa+sw), fewer than 2^24 quarter-units for these K, so the
+    matrix instruction's float32 sums are exact in any order: Y must be exactly
+    bf16(sum_k x_k w_k), the float64 product rounded once."""
+    import torch
+    import quantized_gemm_amd as q
+    say(f"[mxfp4 exact] M={M} K={K} N={N} 2^{sa} 2^{sw}")
+    rng = np.random.default_rng(M + K + N)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.5, -1, -1.5, -2, -3, -4, -6])
+    a = grid[rng.integers(0, len(grid), size=(M, K))]
+    b = grid[rng.integers(0, len(grid), size=(K, N))]
+    a.reshape(M, K // 32, 32)[:, :, 3] = 6 * np.where(rng.random((M, K // 32)) < 0.5, -1, 1)
+    b.reshape(K // 32, 32, N)[:, 11, :] = 6 * np.where(rng.random((K // 32, N)) < 0.5, -1, 1)
+    x = np.ldexp(a, sa).astype(np.float32)
+    w = np.ldexp(b, sw).astype(np.float32)
+    xb = synth.bf16_bits_from_f32(x)
+    assert np.array_equal(synth.f32_from_bf16_bits(xb), x)
+    pw, psw = q.svdq_pack_weights(q.SVDQ_FMT_MXFP4_E8M0SCALE, w)
+    assert np.all(psw == sw + 127)
+    gq, gs = Guarded((K // 64, M, 32), torch.uint8, gpu), Guarded((K // 64, M, 2), torch.uint8, gpu)
+    gy = Guarded((M, N), torch.bfloat16, gpu)
+    qact, ascale, _ = q.svdq_quantize_act_mxfp4(to_dev_bf16(xb, gpu), None, None, gq.tensor, gs.tensor, None)
+    y = q.svdq_linear_mxfp4(qact, ascale, to_dev(pw, gpu), to_dev(psw, gpu), None, None, None, gy.tensor)
+    for g, what in ((gq, "qact"), (gs, "ascale"), (gy, "y")):
+        g.check(what)
+    assert np.all(ascale.cpu().numpy() == sa + 127), "activation scales differ"
+    assert np.array_equal(oracle.e2m1_decode(decode_mx_codes(qact.cpu().numpy(), M, K)), a), "codes differ"
+    ref = oracle.bf16_round((a.astype(np.float64) @ b.astype(np.float64)) * 2.0 ** (sa + sw))
+    got = bf16_to_np(y)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:3].tolist()}"

@@ -173,6 +173,59 @@ def test_w4a4_small_shapes(gpu, M, K, N, rank):
     assert np.array_equal(got, oracle.group_sums(p["qa"], p["qw"]))
 
 
+# (M, K, N, ka, kw): ragged token and column counts, 2 to 8 groups, and the FLUX token count and
+# hidden size (all 48 groups of K = 3072, 24-token quantizer blocks); activation scale 2^-ka, weight
+# scale 2^-kw
+EXACT_SHAPES = [(200, 512, 272, 3, 5), (129, 128, 160, 0, 0), (33, 320, 48, 7, 2), (4100, 256, 144, 4, 6),
+                (4608, 3072, 384, 2, 3)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M,K,N,ka,kw", EXACT_SHAPES, ids=[f"M{m}K{k}N{n}" for m, k, n, _, _ in EXACT_SHAPES])
+def test_product_kernel_exact_with_power_of_two_scales(gpu, M, K, N, ka, kw):
+    """The product kernel itself (scale loads, rescale FMAs, epilogue and store), not its debug
+    instantiation, checked bit for bit. With every group's activation scale 2^-ka and weight scale
+    2^-kw, each rescaled group sum 256 P[g] 2^-(ka+kw) and their running float32 sum stay exact
+    while |sum 256 P| < 2^24 units of 2^-(ka+kw): codes in [-7, 7] up to 8 groups, in [-3, 3] (and
+    one +-7 per group) beyond. Y must then be exactly bf16(2^-(ka+kw) * sum_g P[g]): the integer
+    product, scaled and rounded once."""
+    import torch
+    import quantized_gemm_amd as q
+    say(f"[exact product] M={M} K={K} N={N} 2^-{ka} 2^-{kw}")
+    G = K // 64
+    c = 7 if G <= 8 else 3
+    assert G * (63 * c * c + 49) * 256 < 2 ** 24, "partial sums would not be exact"
+    rng = np.random.default_rng(M * 7 + K + N)
+    qa = rng.integers(-c, c + 1, size=(M, G, 64))
+    qw = rng.integers(-c, c + 1, size=(G, 64, N))
+    # a +-7 in every group, so absmax / 7 is exactly the power of two
+    qa[:, :, 5] = 7 * np.where(rng.random((M, G)) < 0.5, -1, 1)
+    qw[:, 9, :] = 7 * np.where(rng.random((G, N)) < 0.5, -1, 1)
+    qa = qa.reshape(M, K)
+    qw = qw.reshape(K, N)
+    x_bits = synth.bf16_bits_from_f32((qa * 2.0 ** -ka).astype(np.float32))
+    w = (qw * 2.0 ** -kw).astype(np.float32)
+    pw, psw = q.svdq_pack_weights(q.SVDQ_FMT_W4A4_F32SCALE, w)
+    assert np.all(psw == np.float32(2.0 ** -kw))
+    gq = Guarded((G, M, 32), torch.uint8, gpu)
+    gs = Guarded((G, M), torch.float32, gpu)
+    gy = Guarded((M, N), torch.bfloat16, gpu)
+    qact, ascale, _ = q.svdq_quantize_act(to_dev_bf16(x_bits, gpu), None, None, gq.tensor, gs.tensor, None)
+    y = q.svdq_linear_w4a4(qact, ascale, to_dev(pw, gpu), to_dev(psw, gpu), None, None, None, gy.tensor)
+    for g, what in ((gq, "qact"), (gs, "ascale"), (gy, "y")):
+        g.check(what)
+    assert np.array_equal(decode_qact(qact.cpu().numpy(), M, K), qa), "activation codes differ"
+    assert np.all(ascale.cpu().numpy() == np.float32(2.0 ** -ka)), "activation scales differ"
+    if G <= 8:
+        total = oracle.group_sums(qa, qw).sum(axis=0).astype(np.float64)
+    else:  # the same integers through a float64 product (every partial sum below 2^53 is exact)
+        total = qa.astype(np.float64) @ qw.astype(np.float64)
+    ref = oracle.bf16_round(total * 2.0 ** -(ka + kw))
+    got = bf16_to_np(y)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:3].tolist()}"
+
+
 def test_tiny_full_group_sums(gpu):
     import quantized_gemm_amd as q
     p = w4a4_problem("tiny")
