@@ -510,6 +510,46 @@ def test_w4a16_parity(gpu, M, with_bias):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
+# (M, K, N, kx, kw): the adaLN projection, an odd group count with several row tiles, a three-pass grid
+W4A16_EXACT = [(16, 3072, 18432, -2, -6), (5, 1600, 2000, 0, -3), (40, 1024, 8192, -4, 1), (2, 192, 45104, 3, -9)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M,K,N,kx,kw", W4A16_EXACT, ids=[f"M{m}K{k}N{n}" for m, k, n, _, _ in W4A16_EXACT])
+def test_w4a16_exact_with_grid_inputs(gpu, M, K, N, kx, kw):
+    """Kernel (c) checked bit for bit. Activations are integers in [-8, 8] times 2^kx, weights codes in
+    [-7, 7] times 2^kw with a +-7 in every group (so the bf16 scale is exactly 2^kw), the bias an
+    integer times 2^(kx+kw). Then every step is exact: the bf16 products x (128 + u) and their float32
+    sums (per group at most 136 * 512 + 64 * 8 * 143 units of 2^kx), the correction -136 * sum x, the
+    power-of-two rescale and the running sum over K (at most 8 * 7 * K units of 2^(kx+kw)), and the
+    bias add, all below 2^24 units. Y must be exactly bf16(x @ w + b)."""
+    import torch
+    import quantized_gemm_amd as q
+    say(f"[w4a16 exact] M={M} K={K} N={N} 2^{kx} 2^{kw}")
+    assert 8 * 7 * K + 50 < 2 ** 24
+    rng = np.random.default_rng(M + K + N)
+    xi = rng.integers(-8, 9, size=(M, K))
+    code = rng.integers(-7, 8, size=(K // 64, 64, N))
+    code[:, 17, :] = 7 * np.where(rng.random((K // 64, N)) < 0.5, -1, 1)
+    code = code.reshape(K, N)
+    bi = rng.integers(-50, 51, size=N)
+    x = np.ldexp(xi.astype(np.float64), kx).astype(np.float32)
+    w = np.ldexp(code.astype(np.float64), kw).astype(np.float32)
+    b = np.ldexp(bi.astype(np.float64), kx + kw).astype(np.float32)
+    xb, bb = synth.bf16_bits_from_f32(x), synth.bf16_bits_from_f32(b)
+    assert np.array_equal(synth.f32_from_bf16_bits(xb), x) and np.array_equal(synth.f32_from_bf16_bits(bb), b)
+    qw, sc = q.svdq_pack_weights(q.SVDQ_FMT_W4A16_BF16SCALE, w)
+    assert np.all(synth.f32_from_bf16_bits(sc) == np.float32(2.0 ** kw))
+    gy = Guarded((M, N), torch.bfloat16, gpu)
+    y = q.awq_linear_w4a16(to_dev_bf16(xb, gpu), to_dev(qw, gpu), to_dev_bf16(sc, gpu), to_dev_bf16(bb, gpu),
+                           gy.tensor)
+    gy.check("y")
+    ref = oracle.bf16_round(np.ldexp((xi.astype(np.float64) @ code.astype(np.float64)) + bi, kx + kw))
+    got = bf16_to_np(y)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:3].tolist()}"
+
+
 @pytest.mark.parametrize("M,K,N", [(20, 448, 592), (16, 6400, 96), (300, 192, 256), (3, 64, 16),
                                    (3, 128, 24576), (2, 192, 45104)])
 def test_w4a16_shapes(gpu, M, K, N):
