@@ -226,6 +226,47 @@ def test_product_kernel_exact_with_power_of_two_scales(gpu, M, K, N, ka, kw):
     assert bad.size == 0, f"{len(bad)} outputs differ, first at {bad[:3].tolist()}"
 
 
+# (M, K, r): 16-token blocks (r = 16, and M 100), 24-token blocks (r = 32, 48, 64 at M 4608 and a
+# ragged 4100), 32-token blocks (r = 128, 256)
+T_EXACT = [(100, 3072, 16), (4608, 3072, 32), (4100, 1600, 48), (4608, 3072, 64), (4113, 3072, 128),
+           (4608, 3072, 256)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M,K,r", T_EXACT, ids=[f"M{m}K{k}r{r}" for m, k, r in T_EXACT])
+def test_down_projection_exact_with_grid_inputs(gpu, M, K, r):
+    """The fused down projection of kernel (a) checked bit for bit: with X integers in [-8, 8] times
+    2^-3, no smoothing and L1 integers in [-4, 4] times 2^-5, the bf16 operands are exact, every
+    float32 sum of the MFMAs and of the fixed-order reduction over the waves is an integer multiple of
+    2^-8 below 32 K of them (< 2^24), so T must be exactly bf16(X L1). The codes and scales of the same
+    launch are checked against the oracle."""
+    import torch
+    import quantized_gemm_amd as q
+    say(f"[down projection exact] M={M} K={K} r={r}")
+    assert 32 * K < 2 ** 24
+    rng = np.random.default_rng(M + K + r)
+    xi = rng.integers(-8, 9, size=(M, K))
+    li = rng.integers(-4, 5, size=(K, r))
+    x = np.ldexp(xi.astype(np.float64), -3).astype(np.float32)
+    l1 = np.ldexp(li.astype(np.float64), -5).astype(np.float32)
+    l2 = np.zeros((r, 16), np.float32)
+    xb = synth.bf16_bits_from_f32(x)
+    l1t, _ = q.svdq_pack_lowrank(l1, l2)
+    gq, gs = Guarded((K // 64, M, 32), torch.uint8, gpu), Guarded((K // 64, M), torch.float32, gpu)
+    gt = Guarded((M, r), torch.bfloat16, gpu)
+    qact, ascale, t = q.svdq_quantize_act(to_dev_bf16(xb, gpu), None, to_dev_bf16(l1t, gpu), gq.tensor, gs.tensor,
+                                          gt.tensor)
+    for g, what in ((gq, "qact"), (gs, "ascale"), (gt, "lora_act")):
+        g.check(what)
+    qa_ref, sa_ref = oracle.quantize_activations(x, np.ones(K, np.float32))[:2]
+    assert np.array_equal(decode_qact(qact.cpu().numpy(), M, K), qa_ref), "activation codes differ"
+    assert np.array_equal(ascale.cpu().numpy().view(np.uint32), np.ascontiguousarray(sa_ref).view(np.uint32))
+    ref = oracle.bf16_round(np.ldexp(xi.astype(np.float64) @ li.astype(np.float64), -8))
+    got = bf16_to_np(t)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} T values differ, first at {bad[:3].tolist()}"
+
+
 def test_tiny_full_group_sums(gpu):
     import quantized_gemm_amd as q
     p = w4a4_problem("tiny")
