@@ -173,22 +173,25 @@ def test_w4a4_small_shapes(gpu, M, K, N, rank):
     assert np.array_equal(got, oracle.group_sums(p["qa"], p["qw"]))
 
 
-# (M, K, N, ka, kw): ragged token and column counts, 2 to 8 groups, and the FLUX token count and
+# (M, K, N, ka, kw, r): ragged token and column counts, 2 to 8 groups, and the FLUX token count and
 # hidden size (all 48 groups of K = 3072, 24-token quantizer blocks); activation scale 2^-ka, weight
-# scale 2^-kw
-EXACT_SHAPES = [(200, 512, 272, 3, 5), (129, 128, 160, 0, 0), (33, 320, 48, 7, 2), (4100, 256, 144, 4, 6),
-                (4608, 3072, 384, 2, 3)]
+# scale 2^-kw; low-rank rank r (0: no branch and no bias)
+EXACT_SHAPES = [(200, 512, 272, 3, 5, 32), (129, 128, 160, 0, 0, 0), (33, 320, 48, 7, 2, 256),
+                (4100, 256, 144, 4, 6, 16), (4608, 3072, 384, 2, 3, 32)]
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("M,K,N,ka,kw", EXACT_SHAPES, ids=[f"M{m}K{k}N{n}" for m, k, n, _, _ in EXACT_SHAPES])
-def test_product_kernel_exact_with_power_of_two_scales(gpu, M, K, N, ka, kw):
+@pytest.mark.parametrize("M,K,N,ka,kw,r", EXACT_SHAPES,
+                         ids=[f"M{m}K{k}N{n}r{r}" for m, k, n, _, _, r in EXACT_SHAPES])
+def test_product_kernel_exact_with_power_of_two_scales(gpu, M, K, N, ka, kw, r):
     """The product kernel itself (scale loads, rescale FMAs, epilogue and store), not its debug
     instantiation, checked bit for bit. With every group's activation scale 2^-ka and weight scale
     2^-kw, each rescaled group sum 256 P[g] 2^-(ka+kw) and their running float32 sum stay exact
     while |sum 256 P| < 2^24 units of 2^-(ka+kw): codes in [-7, 7] up to 8 groups, in [-3, 3] (and
-    one +-7 per group) beyond. Y must then be exactly bf16(2^-(ka+kw) * sum_g P[g]): the integer
-    product, scaled and rounded once."""
+    one +-7 per group) beyond. The epilogue's low-rank product T L2 (T integers in [-8, 8] times
+    2^-ka, L2 integers in [-4, 4] times 2^-kw) and the bias (integers times 2^-(ka+kw)) add exactly
+    in the same units. Y must then be exactly bf16(2^-(ka+kw) * (sum_g P[g] + T_int L2_int + b_int)):
+    the integer result, scaled and rounded once."""
     import torch
     import quantized_gemm_amd as q
     say(f"[exact product] M={M} K={K} N={N} 2^-{ka} 2^-{kw}")
@@ -211,7 +214,18 @@ def test_product_kernel_exact_with_power_of_two_scales(gpu, M, K, N, ka, kw):
     gs = Guarded((G, M), torch.float32, gpu)
     gy = Guarded((M, N), torch.bfloat16, gpu)
     qact, ascale, _ = q.svdq_quantize_act(to_dev_bf16(x_bits, gpu), None, None, gq.tensor, gs.tensor, None)
-    y = q.svdq_linear_w4a4(qact, ascale, to_dev(pw, gpu), to_dev(psw, gpu), None, None, None, gy.tensor)
+    ti = rng.integers(-8, 9, size=(M, r))
+    li = rng.integers(-4, 5, size=(r, N))
+    bi = rng.integers(-50, 51, size=N)
+    t_dev = l2t_dev = b_dev = None
+    if r:
+        def grid(v, e):
+            return np.ldexp(v.astype(np.float64), e).astype(np.float32)
+        _, l2t = q.svdq_pack_lowrank(np.zeros((K, r), np.float32), grid(li, -kw))
+        l2t_dev = to_dev_bf16(l2t, gpu)
+        t_dev = to_dev_bf16(synth.bf16_bits_from_f32(grid(ti, -ka)), gpu)
+        b_dev = to_dev_bf16(synth.bf16_bits_from_f32(grid(bi, -(ka + kw))), gpu)
+    y = q.svdq_linear_w4a4(qact, ascale, to_dev(pw, gpu), to_dev(psw, gpu), t_dev, l2t_dev, b_dev, gy.tensor)
     for g, what in ((gq, "qact"), (gs, "ascale"), (gy, "y")):
         g.check(what)
     assert np.array_equal(decode_qact(qact.cpu().numpy(), M, K), qa), "activation codes differ"
@@ -220,6 +234,8 @@ def test_product_kernel_exact_with_power_of_two_scales(gpu, M, K, N, ka, kw):
         total = oracle.group_sums(qa, qw).sum(axis=0).astype(np.float64)
     else:  # the same integers through a float64 product (every partial sum below 2^53 is exact)
         total = qa.astype(np.float64) @ qw.astype(np.float64)
+    if r:
+        total = total + ti.astype(np.float64) @ li.astype(np.float64) + bi
     ref = oracle.bf16_round(total * 2.0 ** -(ka + kw))
     got = bf16_to_np(y)
     bad = np.argwhere(got != ref)
