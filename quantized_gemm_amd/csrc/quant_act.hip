@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const
                                                                      uint16_t* __restrict__ tout) {
   static_assert(TT == 1 || TT == 2, "one or two token tiles per block");
   static_assert(AHEAD >= 1 && AHEAD <= kQaChunk, "loads run at most one chunk ahead");
-  static_assert(!HALF || (TT == 2 && FMT == 0), "a half last tile only in two-tile INT4 blocks");
+  static_assert(!HALF || TT == 2, "a half last tile only in two-tile blocks");
   constexpr int kTok = 16 * TT - (HALF ? 8 : 0);
   constexpr int kNR = NR > 0 ? NR : 1;
   // L1 operand tiles in flight per group: all of them with one token tile; with two token tiles
@@ -153,10 +153,17 @@ __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const
         }
         const int mh0 = mh[tt][0];
         const bool ok0 = ok[tt][0];
-        const float s0 = div7(group_max8(am0));
         uint32_t w0;
-        quantize8x1(xh, s0, w0);
-        if (c == 0 && ok0) ascale[(size_t)g * M + mh0] = s0;
+        if constexpr (FMT == 0) {
+          const float s0 = div7(group_max8(am0));
+          quantize8x1(xh, s0, w0);
+          if (c == 0 && ok0) ascale[(size_t)g * M + mh0] = s0;
+        } else {
+          uint32_t b0;
+          quantize_mx8x1(xh, am0, w0, b0);
+          // lanes c == 0, 4 store the E8M0 bytes of blocks 0, 1 of token mh0
+          if ((c & 3) == 0 && ok0) reinterpret_cast<uint8_t*>(ascale)[((size_t)g * M + mh0) * 2 + (c >> 2)] = (uint8_t)b0;
+        }
         if (ok0) *reinterpret_cast<uint32_t*>(qact + ((size_t)g * M + mh0) * 32 + 4 * c) = w0;
         if constexpr (NR > 0) {
           // rows 8..15 of this tile's operand slice keep stale values: they only reach MFMA rows
@@ -359,17 +366,18 @@ int device_cus() {
 //     operand load serves both tiles (half the L1 traffic). M = 4608: r = 128 28.8 -> 21.3 us,
 //     r = 256 44.0 -> 31.3 us, r = 32 16.2 -> 15.0 us; at r = 0 and r = 16 one tile stays faster
 //     (r = 16: 13.6 against 14.7 us).
-//   * For r = 32 .. 64 (INT4), 24-token blocks (the second tile holds 8 tokens) while they still
+//   * For r = 32 .. 64, 24-token blocks (the second tile holds 8 tokens) while they still
 //     fit one per CU: a block's time follows its 8-token rows of vector work (two rows ~10.6 us,
 //     four ~15 us at K = 3072), so three rows on more CUs beat four on fewer. r = 32: M = 4608
-//     15.1 -> 13.8 us, M = 6000 15.7 -> 14.7 us; r = 64, M = 4608: 18.8 -> 18.1 us. At r >= 128
-//     the gain is at most 3% and at M = 6000, r = 128 it is a loss, so those keep 32 tokens.
+//     15.1 -> 13.8 us, M = 6000 15.7 -> 14.7 us; r = 64, M = 4608: 18.8 -> 18.1 us; the MXFP4 rule
+//     at r = 32, M = 4608: 14.5 -> 13.1 us. At r >= 128 the gain is at most 3% and at M = 6000,
+//     r = 128 it is a loss, so those keep 32 tokens.
 template <int NR, int FMT>
 hipError_t launch_rank(const uint16_t* x, int M, int K, const float* inv, const uint16_t* l1t, int r, uint8_t* qact,
                        float* ascale, uint16_t* t, hipStream_t stream) {
   if constexpr (NR > 0) {
     if (NR >= 2 && (M + 15) / 16 > device_cus()) {
-      if constexpr (FMT == 0 && NR >= 2 && NR <= 4) {
+      if constexpr (NR >= 2 && NR <= 4) {
         if ((M + 23) / 24 <= device_cus())
           return launch_nr<NR, FMT, 2, 1, 2, true>(x, M, K, inv, l1t, r, qact, ascale, t, stream);
       }

@@ -140,6 +140,18 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float a) {
 // 2^-e = 1/X as a float for a scale byte (exponent field 254 - byte: always a normal number).
 __device__ __forceinline__ float mx_inv_scale(uint32_t byte) { return __uint_as_float((254u - byte) << 23); }
 
+// MXFP4 of one run of 8 values (xh[0..7], one token, inside one block of 32): packed codes and the
+// E8M0 byte, for the half token tile of a block whose last tile holds 8 tokens.
+__device__ __forceinline__ void quantize_mx8x1(const float (&xh)[8], float am0, uint32_t& w0, uint32_t& b0) {
+  b0 = mx_scale_byte(block_max4(am0));
+  const float i0 = mx_inv_scale(b0);
+  w0 = 0u;
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[0] * i0, xh[1] * i0, 1.0f, 0);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[2] * i0, xh[3] * i0, 1.0f, 1);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[4] * i0, xh[5] * i0, 1.0f, 2);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[6] * i0, xh[7] * i0, 1.0f, 3);
+}
+
 // MXFP4 of the lane's two runs of 8 values (token 0: xh[0..7], token 1: xh[8..15]), each inside one
 // block of 32: packed codes (element e in bits 4e..4e+3) and the two E8M0 bytes.
 __device__ __forceinline__ void quantize_mx8x2(const float (&xh)[16], float am0, float am1, uint32_t& w0,

@@ -29,9 +29,8 @@ def resources():
 def test_every_kernel_instantiation_reported(resources):
     count = lambda src: sum(1 for r in resources if r[0] == src)
     # quantizer, for INT4 and for MXFP4: one 16-token-block instantiation per rank r = 16 q,
-    # q = 0..16, and a 32-token-block one per rank r > 0; for INT4 also a 24-token-block one per
-    # rank r = 32, 48, 64
-    assert count("quant_act.hip") == (17 + 16) * 2 + 3
+    # q = 0..16, a 32-token-block one per rank r > 0 and a 24-token-block one per rank r = 32, 48, 64
+    assert count("quant_act.hip") == (17 + 16 + 3) * 2
     # GEMM: the debug dump and the down-projection partial sum in the dispatch unit, and the
     # 17 ranks x 4 epilogues in the generated units
     assert count("w4a4_gemm.hip") == 2
