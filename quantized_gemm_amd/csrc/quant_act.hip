@@ -110,6 +110,12 @@ __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const
   uint8_t* tb = lds + wave * 16 * TT * kTPitch;
   const uint32_t tw = rr * kTPitch + 16 * c;                       // + (16 tt + 8 hf) rows
   const uint32_t trd = (lane & 15) * kTPitch + 16 * (lane >> 4);  // + 16 tt rows, + 64 for 32 + 8j
+  if constexpr (HALF && NR > 0) {
+    // Rows 8..15 of the half tile's slice are never written; the MFMA reads them into output rows
+    // that are not stored. Zero them once so every value the kernel computes is defined.
+    uint8_t* z = tb + (16 * (TT - 1) + 8) * kTPitch;
+    for (int o = 16 * lane; o < 8 * kTPitch; o += 16 * kWave) *reinterpret_cast<uint4*>(z + o) = uint4{0u, 0u, 0u, 0u};
+  }
 
   v4f tacc[TT][kNR];
 #pragma unroll
@@ -166,8 +172,8 @@ __global__ __launch_bounds__(kQaWaves * 64, MINW) void quantize_act_kernel(const
         }
         if (ok0) *reinterpret_cast<uint32_t*>(qact + ((size_t)g * M + mh0) * 32 + 4 * c) = w0;
         if constexpr (NR > 0) {
-          // rows 8..15 of this tile's operand slice keep stale values: they only reach MFMA rows
-          // (tokens of the next block) whose T is not stored
+          // rows 8..15 of this tile's operand slice stay zero: they only reach MFMA rows whose T is
+          // not stored
           *reinterpret_cast<uint4*>(tb + tw + 16 * tt * kTPitch) =
               uint4{pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]), pack_bf16x2(xh[4], xh[5]),
                     pack_bf16x2(xh[6], xh[7])};
