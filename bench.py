@@ -14,7 +14,9 @@ Prints one JSON line. ``value`` = algorithmic operations of the step / step time
 dense int8 MFMA peak. The timed region holds no event; after it, ``--gemm-samples`` more steps
 (default 200) each bracket their GEMM with HIP events on the launch stream, so the GEMM is sampled
 in the same context as in the timed steps. The per-kernel rates of (a) and (c), and the GEMM
-alone, are measured after that, each kernel back to back over the rotating buffers.
+alone, are measured before the warmup steps (after one pass of the step over every buffer set),
+each kernel back to back over the rotating buffers; that work also brings the GPU to its working
+clock, so a short timed region after a few warmup steps measures the steady state.
 
 ``--all-configs`` reports every configuration (attn, up, down, QKV at r = 32/128/256, W4A16) and
 the unit microbenchmarks (pure matrix-core and vector rates at the observed clock);
@@ -982,6 +984,18 @@ def main():
         print(json.dumps({"only": args.only, "us": t}), flush=True)
         return
 
+    # Per-kernel rates, each kernel alone, back to back over the rotating buffers (after one pass of
+    # the step over every buffer set). They run before the warmup steps, so the timed steps start on a
+    # GPU at its working clock: after the idle set-up, 20 steps behind only 5 warmup steps measured
+    # ~360 us per step against ~297 us behind 100 warmup steps (and ~288 us over 1000 steps).
+    for s in range(R):
+        step(s)
+    t_a = batch_timing(lambda s: q.svdq_quantize_act(xs[s % R], inv, l1t_d, qact[s % R], asc[s % R], tl[s % R],
+                                                     stream=sh), stream)
+    t_c = batch_timing(lambda s: q.awq_linear_w4a16(ax, aqws[s % R], ascl_d, None, ay, stream=sh), stream, 500)
+    t_b_alone = batch_timing(lambda s: q.svdq_linear_w4a4(qact[s % R], asc[s % R], qw_d, sw_d, tl[s % R], l2t_d,
+                                                          bias_d, y, stream=sh), stream)
+
     log(f"[bench] warmup {args.warmup}")
     for s in range(args.warmup):
         step(s)
@@ -1021,12 +1035,6 @@ def main():
     tb_samples = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
     t_b = float(np.median(tb_samples)) * 1e-3  # ms
 
-    # Per-kernel rates, each kernel alone, back to back over the rotating buffers.
-    t_a = batch_timing(lambda s: q.svdq_quantize_act(xs[s % R], inv, l1t_d, qact[s % R], asc[s % R], tl[s % R],
-                                                     stream=sh), stream)
-    t_c = batch_timing(lambda s: q.awq_linear_w4a16(ax, aqws[s % R], ascl_d, None, ay, stream=sh), stream, 500)
-    t_b_alone = batch_timing(lambda s: q.svdq_linear_w4a4(qact[s % R], asc[s % R], qw_d, sw_d, tl[s % R], l2t_d,
-                                                          bias_d, y, stream=sh), stream)
 
     gemm_ops = 2.0 * M * N * K
     lr_flops = 2.0 * M * r * (K + N)
@@ -1075,7 +1083,7 @@ def main():
             "layer_TOPS_a_plus_b": round(gemm_ops / ((t_a["median"] * 1e-3 + t_b) * 1e-3) / 1e12, 2),
             "timing": f"GEMM: HIP events around the GEMM of {len(tb_samples)} steps after the timed region "
                       f"(median); '_alone': the GEMM back to back; quantizer and W4A16: each alone, back to back "
-                      f"over the rotating buffers, 10 batches (median of the batch means)",
+                      f"over the rotating buffers, 10 batches (median of the batch means), before the warmup steps",
             "batches": {"quantize_act": t_a, "linear_w4a4_alone": t_b_alone, "awq_linear_w4a16": t_c},
         },
     }
